@@ -1,0 +1,235 @@
+/*
+ * zero_shard.h — C ABI of one rank's sharded mixed-precision Adam/AdamW step
+ * (ZeRO-DP stage 1/2: optimizer states P_os, + gradients P_os+g) on MI355X.
+ *
+ * The operation (handbook chapter "ZeRO 与 FSDP：切分优化器状态、梯度与参数",
+ * section "从零实现 ZeRO 的 Adam", zero_adam.py): parameters are flattened into
+ * one zero-padded vector split into N equal contiguous shards; rank r receives
+ * the SUM over ranks of the gradient of its shard (reduce-scatter), divides by
+ * N, runs Adam on its fp32 master copy and moments, and the updated shards are
+ * all-gathered back into full parameters.  Mixed precision ("PaddlePaddle
+ * ZeRO优化…", section "混合精度才是最佳拍档"; "论文专题讲解：ZeRO…", section
+ * "显存账") adds 16-bit gradients and parameters, loss-scale unscaling and a
+ * skipped step when a gradient overflows.
+ *
+ * On one GPU the reduce-scatter's input is emulated by N gradient slices of the
+ * rank's shard held in device memory (slice k = rank k's gradient of this shard);
+ * the step writes the rank's new 16-bit parameters into its slots of the full
+ * gather buffer, which is the payload an all-gather would move.
+ *
+ * Conventions shared by every call:
+ *  - All functions return ZERO_OK (0) or a negative ZERO_E* code and never
+ *    throw.  On an error nothing is enqueued and no memory is written; the
+ *    message is available from zero_last_error() on the calling thread.
+ *  - Device pointers are plain device addresses owned by the caller.  The
+ *    library never allocates device memory.  The plan is host memory owned by
+ *    the library (zero_plan ... zero_plan_free).
+ *  - Device work is enqueued on the caller's stream `stream` (a hipStream_t;
+ *    NULL = the null stream) and is asynchronous: flags, norms and coefficients
+ *    land in device memory and are read by the caller after its own sync.
+ *  - "Local" arrays have the rank's shard length S = zero_plan_shard_numel():
+ *    the rank's pieces of every bucket, concatenated in bucket order.  They must
+ *    be 16-byte aligned (ZERO_EALIGN otherwise).  The gather buffer needs only
+ *    element alignment.
+ *  - Floating point: every operation of the step is one IEEE fp32 rounding (no
+ *    contraction into fused multiply-add, correctly rounded division and square
+ *    root, denormals kept); 16-bit results are rounded to nearest, ties to even.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ZERO_OK = 0,
+  ZERO_EINVAL = -1, /* bad argument: null pointer, range, dtype, aliasing, size */
+  ZERO_EALIGN = -2, /* a local array or slice is not 16-byte aligned */
+  ZERO_ENOMEM = -3, /* host allocation of the plan failed */
+  ZERO_EHIP = -4    /* the HIP runtime reported an error (code in the message) */
+};
+
+typedef enum { ZERO_F32 = 0, ZERO_BF16 = 1, ZERO_F16 = 2 } zero_dtype_t;
+
+typedef struct zero_plan zero_plan_t;
+
+/* ------------------------------------------------------------------------ */
+/* Planner (host only, exact integer arithmetic)                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Build the flat layout of `n_tensors` tensors of sizes numel[0..n_tensors-1]
+ * (taken in list order) over `world` = N ranks (zero_adam.py: flatten, pad to
+ * ceil(numel/N)*N, rank r owns [r*S, (r+1)*S)).
+ *
+ * bucket_cap <= 0: one bucket, exactly that flat vector.  bucket_cap > 0:
+ * tensors are packed greedily in order into buckets (a bucket is closed when the
+ * next tensor would take it past the cap; a tensor larger than the cap sits
+ * alone), the constant-size buffers of ZeRO-R (C_B); each bucket b of B_b
+ * elements is padded to P_b = N * S_b, S_b = ceil(B_b / N), and rank r's piece
+ * of it sits at base_b + r * S_b in the gather buffer.
+ *
+ * numel: host array, each >= 0, sum > 0.  world >= 1.  *out receives the plan.
+ * Errors: ZERO_EINVAL (bad sizes), ZERO_ENOMEM.
+ */
+int zero_plan(const int64_t* numel, int32_t n_tensors, int32_t world, int64_t bucket_cap,
+              zero_plan_t** out);
+
+/* Free a plan (NULL is ignored). */
+void zero_plan_free(zero_plan_t* plan);
+
+/* Scalars of a plan; -1 for a NULL plan. */
+int64_t zero_plan_shard_numel(const zero_plan_t* plan);  /* S = sum_b S_b            */
+int64_t zero_plan_total_numel(const zero_plan_t* plan);  /* Psi = sum of numel       */
+int64_t zero_plan_padded_numel(const zero_plan_t* plan); /* gather length sum_b P_b  */
+int32_t zero_plan_world(const zero_plan_t* plan);
+int32_t zero_plan_num_buckets(const zero_plan_t* plan);
+int32_t zero_plan_num_tensors(const zero_plan_t* plan);
+
+/* Bucket b: flat base, element count B_b, padded length P_b, shard S_b, and
+ * the tensors it holds (first index, count).  Any output pointer may be NULL. */
+int zero_plan_bucket(const zero_plan_t* plan, int32_t b, int64_t* base, int64_t* numel,
+                     int64_t* padded, int64_t* shard, int32_t* first_tensor, int32_t* n_tensors);
+
+/* Tensor i: its bucket and the flat (gather-buffer) offset of its first element. */
+int zero_plan_tensor(const zero_plan_t* plan, int32_t i, int32_t* bucket, int64_t* offset);
+
+/*
+ * Rank `rank`'s piece of bucket b: gather_off = base_b + rank*S_b (offset in the
+ * gather buffer), local_off (offset in the rank's local arrays), valid =
+ * clamp(B_b - rank*S_b, 0, S_b) leading non-padding elements.  Piece length is S_b.
+ */
+int zero_plan_rank_segment(const zero_plan_t* plan, int32_t rank, int32_t b, int64_t* gather_off,
+                           int64_t* local_off, int64_t* valid);
+
+/*
+ * Per-device model-state bytes of mixed-precision Adam, K = 12 ("论文专题讲解：ZeRO…",
+ * section "ZeRO-DP 三阶段"; handbook section "三个级别"):
+ *   stage 0: 16 Psi (plain data parallel); 1: 4 Psi + 12 Psi/N; 2: 2 Psi + 14 Psi/N;
+ *   3: 16 Psi / N.
+ * formula_bytes gets the formula with the unpadded Psi; padded_bytes the same
+ * with N*S for Psi and S for Psi/N (the bytes this layout really holds).
+ */
+int zero_plan_bytes(const zero_plan_t* plan, int32_t stage, double* formula_bytes,
+                    int64_t* padded_bytes);
+
+/* ------------------------------------------------------------------------ */
+/* Device operations                                                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Bytes of device workspace that zero_reduce_shard / zero_shard_norm need
+ * (per-workgroup overflow words and float64 partial sums).  Caller-allocated,
+ * 16-byte aligned, no initial content required.  0 for a NULL plan.
+ */
+size_t zero_workspace_bytes(const zero_plan_t* plan);
+
+/*
+ * Gradient preparation, first pass of the clipped step (global-norm clipping
+ * needs the norm of the whole gradient before any element is updated).
+ *
+ * For every local element j < S:
+ *   acc = slice_0[j] + slice_1[j] + ... + slice_{N-1}[j]   (fp32, ascending k)
+ *   g   = (acc / N) * inv_scale                              (zero_adam.py g /= world;
+ *                                                             GradScaler unscale)
+ * Slice k starts at grad + k * grad_ld elements (dtype grad_dtype), ld >= S,
+ * 16-byte aligned start and stride.  If g_out != NULL, g is stored there (fp32,
+ * [S], 16-byte aligned).  Per workgroup, an overflow word (any non-finite g)
+ * and, if want_sumsq, the float64 sum of g^2 go to `ws`
+ * (zero_workspace_bytes).  The partition of elements over workgroups depends
+ * only on S, so the sums are deterministic run to run.
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EHIP.
+ */
+int zero_reduce_shard(const zero_plan_t* plan, const void* grad, int64_t grad_ld,
+                      zero_dtype_t grad_dtype, float inv_scale, float* g_out, void* ws,
+                      int32_t want_sumsq, void* stream);
+
+/*
+ * Second pass (one workgroup): finalize what zero_reduce_shard left in `ws`.
+ *   overflow_out (device u32): 1 if any g was non-finite, else 0.
+ *   q = sum of the partial sums in a fixed order; Q = q + other_ranks_sumsq (the
+ *   other ranks' share of the global sum, 0 on one rank); norm = sqrt(Q) (fp64).
+ *   sumsq_out (device f64, may be NULL): q.
+ *   clip_coef_out (device f32, may be NULL): fp32(max_norm / norm) if
+ *   max_norm > 0 and norm > max_norm, else 1.
+ * Errors: ZERO_EINVAL, ZERO_EHIP.
+ */
+int zero_shard_norm(const zero_plan_t* plan, const void* ws, double other_ranks_sumsq,
+                    float max_norm, uint32_t* overflow_out, double* sumsq_out,
+                    float* clip_coef_out, void* stream);
+
+/* Arguments of zero_adam_step (host struct; pointers are device addresses). */
+typedef struct zero_adam_args {
+  int32_t rank;              /* 0 <= rank < N                                      */
+  /* gradient source: either N slices (fused step) ...                          */
+  const void* grad;          /* slice k at grad + k*grad_ld elements               */
+  int64_t grad_ld;           /* elements, >= S                                     */
+  zero_dtype_t grad_dtype;
+  float inv_scale;           /* fp32(1 / loss scale); 1 without loss scaling       */
+  /* ... or the fp32 gradient written by zero_reduce_shard (then grad is ignored) */
+  const float* g_stash;
+  const float* clip_coef;    /* device f32 multiplier of g_stash, or NULL (= 1)    */
+  /* state, fp32 [S] each                                                       */
+  const float* master_in;
+  const float* m_in;
+  const float* v_in;
+  float* master_out;
+  float* m_out;
+  float* v_out;
+  /* output: full gather buffer (zero_plan_padded_numel elements); only this
+   * rank's pieces are written, every element of them (padding too)          */
+  void* gather;
+  zero_dtype_t param_dtype;
+  /* hyper-parameters (host doubles; rounded once to fp32 inside)               */
+  double lr, beta1, beta2, eps, weight_decay;
+  int64_t step;              /* 1-based index of this step (t after t += 1)       */
+  /* flags (device u32)                                                         */
+  const uint32_t* skip_in;   /* NULL, or: nonzero at run time -> the step writes nothing */
+  uint32_t* overflow_out;    /* fused step: receives 1 if any g is non-finite, else 0   */
+  /* optional hipEvent_t pair recorded around the main update kernel only       */
+  void* ev_begin;
+  void* ev_end;
+} zero_adam_args_t;
+
+/*
+ * The AdamW update of the rank's shard and the write of its gather slots.
+ *
+ * Per element (zero_adam.py step() with decoupled weight decay; constants
+ * computed in float64 and rounded once to fp32: b1, b2, 1-b1, 1-b2,
+ * bc1 = 1-b1^step, bc2 = 1-b2^step, lr, eps, dec = 1-lr*wd):
+ *   g      = fused: (sum_k slice_k / N) * inv_scale   |  stash: g_stash * clip_coef
+ *   m'     = b1*m + (1-b1)*g;     v' = b2*v + (1-b2)*(g*g)
+ *   m_hat  = m'/bc1;  v_hat = v'/bc2;  u = (lr*m_hat) / (sqrt(v_hat) + eps)
+ *   master'= dec*master - u;  gather[slot(j)] = round_to_nearest_even(master')
+ *
+ * Overflow handling (GradScaler skips the optimizer step on inf/NaN):
+ *  - fused mode: the flag is computed in the same pass over the slices.  The
+ *    state outputs must not overlap the inputs (ping-pong buffers; the caller
+ *    swaps them only when *overflow_out == 0 after the step).  If the flag is
+ *    set, the rank's gather slots are rewritten from master_in before the call's
+ *    work completes, so they keep their pre-step values.
+ *  - stash mode: the decision is known beforehand (skip_in = zero_shard_norm's
+ *    overflow_out), so outputs may alias inputs (in place); overflow_out unused.
+ *  - skip_in != NULL and *skip_in != 0 in either mode: nothing is written.
+ * ev_begin/ev_end (hipEvent_t or NULL) are recorded on `stream` immediately
+ * before and after the main update kernel.
+ * Errors: ZERO_EINVAL (incl. overlapping outputs in fused mode), ZERO_EALIGN,
+ * ZERO_EHIP.
+ */
+int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* args, void* stream);
+
+/* Message of the last error on this thread ("" if none). */
+const char* zero_last_error(void);
+
+/* Library version string. */
+const char* zero_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_SHARD_H */

@@ -9,10 +9,11 @@ starting at r * piece.
 Buckets (parity unpinned — the pages only say that real ZeRO-2 reduce-scatters
 gradients bucket by bucket during backward, same section, and that fused
 temporary buffers should have a constant size, "ZeRO-R", C_B): with a positive
-cap, tensors are packed greedily in list order into buckets; a bucket is closed
-when adding the next tensor would take it past the cap, so a tensor larger than
-the cap sits alone.  Each bucket is then laid out exactly like the single flat
-vector above.  A cap <= 0 gives one bucket, i.e. the plain flat vector.
+cap, tensors are packed greedily in list order into buckets; a bucket that
+already holds elements is closed when adding the next tensor would take it past
+the cap, so a tensor larger than the cap sits alone and no bucket is empty
+(zero-size tensors join the open bucket).  Each bucket is then laid out exactly
+like the single flat vector above.  A cap <= 0 gives one bucket, i.e. the plain flat vector.
 
 Byte accounting (section "三个级别" of the same chapter; "ZeRO-DP 三阶段" of the
 paper deep-dive): per-device model state for mixed-precision Adam with K = 12 is
@@ -74,7 +75,7 @@ def make_plan(numels: Sequence[int], world: int, bucket_cap: int = 0) -> Plan:
     cur: List[int] = []
     cur_size = 0
     for i, n in enumerate(numels):
-        if bucket_cap > 0 and cur and cur_size + n > bucket_cap:
+        if bucket_cap > 0 and n > 0 and cur_size > 0 and cur_size + n > bucket_cap:
             groups.append(cur)
             cur, cur_size = [], 0
         cur.append(i)

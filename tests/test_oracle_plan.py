@@ -122,11 +122,12 @@ def _check_invariants(pl, sizes, cap):
         assert b.numel == sum(sizes[b.first_tensor:b.first_tensor + b.n_tensors])
         assert b.padded == pl.world * b.shard and b.shard * pl.world >= b.numel > (b.shard - 1) * pl.world
         if cap > 0:
-            assert b.numel <= cap or b.n_tensors == 1
+            nonzero = sum(1 for n in sizes[b.first_tensor:b.first_tensor + b.n_tensors] if n > 0)
+            assert b.numel <= cap or nonzero == 1
     assert nxt == len(sizes)
     if cap > 0:   # greedy: the next tensor would not have fit
         for b, b2 in zip(pl.buckets, pl.buckets[1:]):
-            assert b.numel + sizes[b2.first_tensor] > cap
+            assert b.numel > 0 and b.numel + sizes[b2.first_tensor] > cap and sizes[b2.first_tensor] > 0
     # tensors tile each bucket's front, padding sits at its end
     for i, n in enumerate(sizes):
         b = pl.buckets[pl.tensor_bucket[i]]
@@ -160,6 +161,13 @@ def _check_invariants(pl, sizes, cap):
 def test_plan_invariants(sizes, world, cap):
     pl = P.make_plan(sizes, world, cap)
     _check_invariants(pl, sizes, cap)
+
+
+def test_zero_size_tensors_never_make_an_empty_bucket():
+    pl = P.make_plan([0, 5, 0, 0, 4, 0], 2, 3)
+    assert [(b.first_tensor, b.n_tensors, b.numel) for b in pl.buckets] == [(0, 4, 5), (4, 2, 4)]
+    assert all(b.shard > 0 for b in pl.buckets)
+    _check_invariants(pl, [0, 5, 0, 0, 4, 0], 3)
 
 
 def test_rank_all_padding():
