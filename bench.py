@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Benchmark: one rank's sharded mixed-precision AdamW step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
+
+A step is one pass of the whole hot path over one rank's shard: reduce the N
+gradient slices, average, unscale, check for overflow (and, for the clipped
+workload, the two-pass global-norm clip), AdamW on the fp32 master/m/v, and the
+rounded parameters written into the rank's slots of the all-gather buffer.
+Inputs are seeded synthetic data resident in HBM before the timed region.
+
+Prints ONE JSON line (the default workload: GPT-2 1.5B shapes, N = 8, rank 7,
+bf16 slices and parameters).  `--workload all` also writes one line per
+workload to stderr (and to --report if given), and prints the default
+workload's line last on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+DEFAULT = "gpt2_1p5b_n8"
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published peak
+METRIC = "shard elements/sec of fused ZeRO AdamW step; achieved HBM GB/s vs peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def round_up(x, m):
+    return (x + m - 1) // m * m
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "abi.cpp", "zero_internal.h"):
+        with open(os.path.join(ROOT, "zero_sharded_mixed_plan_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# the CPU oracle, timed on a bounded sample (cpu_baseline)
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w, slices, state, S, target_s=12.0, max_elems=1 << 26, chunk=1 << 20):
+    import concurrent.futures as cf
+
+    import numpy as np
+    import torch
+
+    from oracle import step as OS
+
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    n = min(S, max_elems)
+    n -= n % chunk if n > chunk else 0
+    n = max(n, min(S, chunk))
+
+    def host(t):
+        t = t.detach().cpu().contiguous()
+        if t.dtype in (torch.bfloat16, torch.float16):
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    sl = [host(slices[k, :n]) for k in range(w.world)]
+    p, m, v = (host(x[:n]) for x in state)
+    kw = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+              t=w.t0 + 1, inv_scale=1.0 / w.loss_scale, max_norm=w.max_norm)
+
+    def work(a):
+        b = min(n, a + chunk)
+        OS.shard_step([s[a:b] for s in sl], w.grad_dtype, w.param_dtype, w.world, p[a:b], m[a:b],
+                      v[a:b], **kw)
+        return b - a
+
+    done = 0
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        while True:
+            done += sum(ex.map(work, range(0, n, chunk)))
+            if time.perf_counter() - t0 >= target_s or done >= 64 * n:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} elements of the rank's shard, stepped {done // n} time(s) "
+                      f"in {chunk}-element chunks on {threads} threads ({dt:.1f} s)"}
+
+
+# ---------------------------------------------------------------------------
+# one workload on the GPU
+# ---------------------------------------------------------------------------
+
+def run(name, steps, warmup, with_cpu):
+    import torch
+
+    import workloads as W
+    import zero_sharded_mixed_plan_amd as Z
+    from zero_sharded_mixed_plan_amd.optim import dtype_code
+
+    w = W.FULL[name]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    plan = Z.Plan(W.numels(w.tensors), w.world, w.bucket_cap)
+    S = plan.shard_numel
+    lay = W.Layout(S=S, segments=plan.segments(w.rank), tensor_flat_off=plan.tensor_offsets())
+    ld = round_up(S, 64)
+    log(f"[bench] {name}: S={S} N={w.world} rank={w.rank} buckets={plan.num_buckets} "
+        f"grads={w.grad_dtype} params={w.param_dtype} clip={w.max_norm}")
+
+    t_gen = time.perf_counter()
+    slices = W.make_slices(w, lay, step=1, ld=ld, device=dev)
+    if w.inject_inf_step is not None:   # time clean steps: draw the slices of a clean step
+        slices = W.make_slices(w, lay, step=w.inject_inf_step + 1, ld=ld, device=dev, out=slices)
+    A = list(W.make_state(w, lay, dev))
+    B = [torch.empty_like(x) for x in A]
+    gather = torch.zeros(plan.padded_numel, dtype=W.torch_dtype(w.param_dtype), device=dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    clip = w.max_norm > 0
+    if clip:
+        g = torch.empty(S, dtype=torch.float32, device=dev)
+        ws = torch.empty(plan.workspace_bytes(), dtype=torch.uint8, device=dev)
+        sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+        coef = torch.zeros(1, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s")
+
+    stream = torch.cuda.current_stream()
+    st = stream.cuda_stream
+    gb = Z.DTYPE_BYTES[dtype_code(W.torch_dtype(w.grad_dtype))]
+    pb = Z.DTYPE_BYTES[dtype_code(W.torch_dtype(w.param_dtype))]
+    common = dict(rank=w.rank, gather=gather.data_ptr(), param_dtype=dtype_code(gather.dtype),
+                  lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+
+    def new_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(stream)       # creates the underlying hipEvent
+        return evs
+
+    state = {"cur": A, "nxt": B, "t": w.t0}
+
+    def step(ev=None):
+        t = state["t"] + 1
+        if clip:
+            e_red0, e_red1, e_up0, e_up1 = ev if ev else (None,) * 4
+            if e_red0 is not None:
+                e_red0.record(stream)
+            Z.zero_reduce_shard(plan, slices.data_ptr(), ld, dtype_code(slices.dtype),
+                                1.0 / w.loss_scale, g.data_ptr(), ws.data_ptr(), True, st)
+            if e_red1 is not None:
+                e_red1.record(stream)
+            Z.zero_shard_norm(plan, ws.data_ptr(), 0.0, w.max_norm, flag.data_ptr(),
+                              sumsq.data_ptr(), coef.data_ptr(), st)
+            p, m, v = state["cur"]
+            a = Z.adam_args(g_stash=g.data_ptr(), clip_coef=coef.data_ptr(), master_in=p.data_ptr(),
+                            m_in=m.data_ptr(), v_in=v.data_ptr(), master_out=p.data_ptr(),
+                            m_out=m.data_ptr(), v_out=v.data_ptr(), skip_in=flag.data_ptr(),
+                            step=t, ev_begin=e_up0.cuda_event if e_up0 else None,
+                            ev_end=e_up1.cuda_event if e_up1 else None, **common)
+            Z.zero_adam_step(plan, a, st)
+        else:
+            e0, e1 = ev if ev else (None, None)
+            src, dst = state["cur"], state["nxt"]
+            a = Z.adam_args(grad=slices.data_ptr(), grad_ld=ld, grad_dtype=dtype_code(slices.dtype),
+                            inv_scale=1.0 / w.loss_scale, master_in=src[0].data_ptr(),
+                            m_in=src[1].data_ptr(), v_in=src[2].data_ptr(),
+                            master_out=dst[0].data_ptr(), m_out=dst[1].data_ptr(),
+                            v_out=dst[2].data_ptr(), overflow_out=flag.data_ptr(), step=t,
+                            ev_begin=e0.cuda_event if e0 else None,
+                            ev_end=e1.cuda_event if e1 else None, **common)
+            Z.zero_adam_step(plan, a, st)
+            # the data are finite, so every step commits: swap without a host read
+            state["cur"], state["nxt"] = dst, src
+        state["t"] = t
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(flag.item()) != 0:
+        raise RuntimeError("warm-up step overflowed on finite synthetic data")
+
+    n_ev = 4 if clip else 2
+    evs = [new_events(n_ev) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if int(flag.item()) != 0:
+        raise RuntimeError("timed step overflowed on finite synthetic data")
+
+    ms_step = wall / steps * 1e3
+    kernels = {}
+    if clip:
+        red = [evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)]
+        upd = [evs[i][2].elapsed_time(evs[i][3]) for i in range(steps)]
+        kernels["reduce_kernel"] = (sum(red) / steps, w.world * gb + 4)
+        kernels["step_kernel_stash"] = (sum(upd) / steps, 4 + 24 + pb)
+    else:
+        upd = [evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)]
+        kernels["step_kernel"] = (sum(upd) / steps, w.world * gb + 24 + pb)
+    dom = max(kernels, key=lambda k: kernels[k][0])
+    k_ms, k_bpe = kernels[dom]
+    achieved = k_bpe * S / (k_ms * 1e-3) / 1e9
+    bpe_total = w.world * gb + 24 + pb + (8 if clip else 0)
+    traffic = load_traffic(dom, name)
+    out = {
+        "metric": METRIC,
+        "value": S / (ms_step * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": name, "shard_elements": S, "world": w.world, "rank": w.rank,
+            "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype, "buckets": plan.num_buckets,
+            "clip": clip, "algorithmic_bytes_per_element": bpe_total,
+            "step_GBps": bpe_total * S / (ms_step * 1e-3) / 1e9,
+            "kernel_ms": {k: round(v[0], 5) for k, v in kernels.items()},
+            "parallelism": "one rank of N (single GPU)",
+        },
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "bytes_per_element": k_bpe,
+                     "traffic": traffic},
+    }
+    if with_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, slices, [x for x in state["cur"]], S)
+    del slices, A, B, gather
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline")
+    ap.add_argument("--report", default=None, help="append every workload's JSON line here")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one rank on one GPU; --gpus {args.gpus} is not "
+              "supported (the multi-GPU collectives are out of scope)", file=sys.stderr)
+        sys.exit(2)
+    import workloads as W
+    names = W.ORDER if args.workload == "all" else [args.workload]
+    if args.workload != "all" and args.workload not in W.FULL:
+        sys.exit(f"unknown workload {args.workload}; one of {W.ORDER} or 'all'")
+    lines = {}
+    for nm in names:
+        res = run(nm, args.steps, args.warmup, with_cpu=(not args.no_cpu and nm == DEFAULT))
+        lines[nm] = res
+        if len(names) > 1:
+            log(json.dumps(res))
+        if args.report:
+            with open(args.report, "a", encoding="utf-8") as f:
+                f.write(json.dumps(res) + "\n")
+    head = lines.get(DEFAULT) or lines[names[-1]]
+    print(json.dumps(head), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -188,8 +188,9 @@ typedef struct zero_adam_args {
   double lr, beta1, beta2, eps, weight_decay;
   int64_t step;              /* 1-based index of this step (t after t += 1)       */
   /* flags (device u32)                                                         */
-  const uint32_t* skip_in;   /* NULL, or: nonzero at run time -> the step writes nothing */
-  uint32_t* overflow_out;    /* fused step: receives 1 if any g is non-finite, else 0   */
+  const uint32_t* skip_in;   /* NULL, or: nonzero at run time -> state is not written   */
+  uint32_t* overflow_out;    /* fused step: 1 if the step was not applied (a non-finite
+                                g, or skip_in set), else 0                              */
   /* optional hipEvent_t pair recorded around the main update kernel only       */
   void* ev_begin;
   void* ev_end;
@@ -214,7 +215,10 @@ typedef struct zero_adam_args {
  *    work completes, so they keep their pre-step values.
  *  - stash mode: the decision is known beforehand (skip_in = zero_shard_norm's
  *    overflow_out), so outputs may alias inputs (in place); overflow_out unused.
- *  - skip_in != NULL and *skip_in != 0 in either mode: nothing is written.
+ *  - skip_in != NULL and *skip_in != 0 in either mode: the state outputs are
+ *    not written; in fused mode with overflow_out, *overflow_out becomes 1 and
+ *    the gather slots are rewritten from master_in (in stash mode they are not
+ *    touched).
  * ev_begin/ev_end (hipEvent_t or NULL) are recorded on `stream` immediately
  * before and after the main update kernel.
  * Errors: ZERO_EINVAL (incl. overlapping outputs in fused mode), ZERO_EALIGN,

@@ -1,0 +1,152 @@
+"""The C ABI on the host: the library loads, exports every declared symbol, its
+planner matches the oracle planner exactly, and bad arguments are rejected
+before anything is enqueued (no GPU is touched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import workloads as W
+import zero_sharded_mixed_plan_amd as Z
+from oracle import plan as OP
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "zero_shard.h"), encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(zero_[a-z_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    declared = _declared_functions()
+    assert len(declared) >= 17
+    L = ctypes.CDLL(Z._abi.LIB_PATH)
+    missing = [n for n in declared if not hasattr(L, n)]
+    assert not missing, missing
+    assert sorted(Z.EXPORTS) == declared
+
+
+CASES = [(W.numels(w.tensors), w.world, w.bucket_cap) for w in W.FULL.values()] + \
+        [(W.numels(w.tensors), w.world, w.bucket_cap) for w in W.SMALL.values()] + [
+    ([3], 4, 0), ([5, 0, 7], 1, 0), ([8, 8], 4, 0), ([10, 30, 5, 5, 1], 3, 12), ([1] * 50, 7, 6),
+    ([0, 5, 0, 0, 4, 0], 2, 3), ([7] * 40, 3, 7), (list(range(1, 300)), 5, 1000),
+]
+
+
+@pytest.mark.parametrize("sizes,world,cap", CASES)
+def test_planner_matches_oracle(sizes, world, cap):
+    o = OP.make_plan(sizes, world, cap)
+    p = Z.Plan(sizes, world, cap)
+    assert p.shard_numel == o.shard_numel
+    assert p.total_numel == o.psi
+    assert p.padded_numel == o.padded_numel
+    assert p.num_buckets == len(o.buckets)
+    assert p.num_tensors == len(sizes)
+    for b, ob in enumerate(o.buckets):
+        assert p.bucket(b) == (ob.base, ob.numel, ob.padded, ob.shard, ob.first_tensor, ob.n_tensors)
+    for i in range(len(sizes)):
+        assert p.tensor(i) == (o.tensor_bucket[i], o.tensor_offset[i])
+    ranks = range(world) if world <= 16 else [0, 1, world // 2, world - 1]
+    for r in ranks:
+        assert p.segments(r) == OP.rank_segments(o, r)
+    for stage in range(4):
+        f, pb = p.bytes(stage)
+        assert pb == OP.padded_model_state_bytes(o, stage)
+        exact = OP.model_state_bytes(sum(sizes), world, stage)
+        assert abs(f - float(exact)) <= 1e-12 * float(exact)
+
+
+@pytest.mark.parametrize("bad", [dict(numels=[], world=2), dict(numels=[0, 0], world=2),
+                                 dict(numels=[4], world=0), dict(numels=[-1, 5], world=2)])
+def test_plan_rejects(bad):
+    with pytest.raises(Z.ZeroError) as e:
+        Z.Plan(bad["numels"], bad["world"])
+    assert e.value.code == Z.ZERO_EINVAL
+    assert "zero_plan" in Z.zero_last_error()
+
+
+def test_accessors_reject_bad_indices():
+    p = Z.Plan([10, 20], 4)
+    for call in (lambda: p.bucket(1), lambda: p.tensor(2), lambda: p.rank_segment(4, 0),
+                 lambda: p.rank_segment(0, -1), lambda: p.bytes(4)):
+        with pytest.raises(Z.ZeroError):
+            call()
+    L = Z.lib()
+    assert L.zero_plan_shard_numel(None) == -1
+    assert L.zero_workspace_bytes(None) == 0
+
+
+# fake, well-aligned device addresses: validation must fail before any use
+BASE = 1 << 40
+
+
+def _good(plan, **over):
+    S = plan.shard_numel
+    a = dict(rank=3, grad=BASE, grad_ld=S + (-S) % 8, grad_dtype=Z.ZERO_BF16,
+             master_in=BASE + (1 << 32), m_in=BASE + (2 << 32), v_in=BASE + (3 << 32),
+             master_out=BASE + (4 << 32), m_out=BASE + (5 << 32), v_out=BASE + (6 << 32),
+             gather=BASE + (7 << 32), param_dtype=Z.ZERO_BF16, lr=1e-3, beta1=0.9, beta2=0.999,
+             eps=1e-8, step=1, overflow_out=BASE + (8 << 32))
+    a.update(over)
+    return Z.adam_args(**a)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(rank=4), Z.ZERO_EINVAL),
+    (dict(rank=-1), Z.ZERO_EINVAL),
+    (dict(master_in=None), Z.ZERO_EINVAL),
+    (dict(gather=None), Z.ZERO_EINVAL),
+    (dict(grad=None), Z.ZERO_EINVAL),
+    (dict(grad_ld=10), Z.ZERO_EINVAL),
+    (dict(grad_dtype=7), Z.ZERO_EINVAL),
+    (dict(param_dtype=9), Z.ZERO_EINVAL),
+    (dict(master_in=BASE + (1 << 32) + 4), Z.ZERO_EALIGN),
+    (dict(grad=BASE + 8), Z.ZERO_EALIGN),
+    (dict(grad_ld=4803), Z.ZERO_EALIGN),                 # 4803 bf16 = 9606 B stride
+    (dict(gather=BASE + (7 << 32) + 1), Z.ZERO_EALIGN),
+    (dict(step=0), Z.ZERO_EINVAL),
+    (dict(beta1=1.0), Z.ZERO_EINVAL),
+    (dict(lr=float("nan")), Z.ZERO_EINVAL),
+    (dict(master_out=BASE + (1 << 32)), Z.ZERO_EINVAL),  # in place with an overflow flag
+    (dict(m_out=BASE + (4 << 32)), Z.ZERO_EINVAL),       # two outputs overlap
+    (dict(gather=BASE + (4 << 32) + 64), Z.ZERO_EINVAL),  # gather overlaps master_out
+    (dict(v_out=BASE + 16), Z.ZERO_EINVAL),              # output overlaps the slices
+])
+def test_step_validation(over, code):
+    plan = Z.Plan(W.numels(W.toy_mlp()), 4)
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_adam_step(plan, _good(plan, **over))
+    assert e.value.code == code, Z.zero_last_error()
+
+
+def test_in_place_allowed_without_flag_or_with_stash():
+    """Exact in-place state is legal when the skip decision does not need the
+    inputs afterwards; partial overlap never is (validated, then rejected only
+    for the deliberately broken cases)."""
+    plan = Z.Plan(W.numels(W.toy_mlp()), 4)
+    part = _good(plan, overflow_out=None, master_out=BASE + (1 << 32) + 16)
+    with pytest.raises(Z.ZeroError):
+        Z.zero_adam_step(plan, part)
+
+
+def test_reduce_and_norm_validation():
+    plan = Z.Plan([100], 4)
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_reduce_shard(plan, BASE, 32, Z.ZERO_BF16, 1.0, 0, 0, True)
+    assert e.value.code == Z.ZERO_EINVAL          # no workspace
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_reduce_shard(plan, BASE + 2, 32, Z.ZERO_BF16, 1.0, 0, BASE, True)
+    assert e.value.code == Z.ZERO_EALIGN
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_reduce_shard(plan, BASE, 16, Z.ZERO_BF16, 1.0, 0, BASE, True)
+    assert e.value.code == Z.ZERO_EINVAL          # ld < S = 25
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_shard_norm(plan, BASE, -1.0, 1.0, 0, 0, 0)
+    assert e.value.code == Z.ZERO_EINVAL
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_shard_norm(plan, BASE, 0.0, float("inf"), 0, 0, 0)
+    assert e.value.code == Z.ZERO_EINVAL

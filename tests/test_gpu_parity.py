@@ -1,0 +1,260 @@
+"""GPU parity of the HIP step against the oracle, through the C ABI, at sizes the
+oracle finishes in seconds (several 2048-element tiles and a ragged tail)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+import zero_sharded_mixed_plan_amd as Z
+from gpu_harness import (CODE, Rig, check_params, compare_step, from_storage, guards, say,
+                         storage)
+from oracle import casts as OC
+from oracle import plan as OP
+from oracle import step as OS
+
+pytestmark = pytest.mark.gpu
+F = np.float32
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _oracle_slices(sl_cpu, S, world):
+    return [storage(sl_cpu[k, :S]) for k in range(world)]
+
+
+def run_workload(w: W.Workload, ld_align=64, rank=None, steps=None):
+    """Run w.steps steps on the GPU and in the oracle; compare everything."""
+    rig = Rig(w, ld_align=ld_align, rank=rank)
+    w = rig.w
+    say(f"workload {w.name} S={rig.S} N={w.world} rank={w.rank} grads={w.grad_dtype} "
+        f"params={w.param_dtype} buckets={len(rig.lay.segments)} ld={rig.ld}")
+    p, m, v = rig.p0, rig.m0, rig.v0
+    gather_ref = rig.gather0.copy()
+    cur, nxt = rig.A, rig.B
+    t = w.t0
+    same = total = 0
+    for step in range(1, (steps or w.steps) + 1):
+        sl_cpu, sl_dev = rig.slices(step)
+        sl = _oracle_slices(sl_cpu, rig.S, w.world)
+        kw = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                  t=t + 1, inv_scale=1.0 / w.loss_scale)
+        if w.max_norm > 0:
+            rig.reduce_norm(sl_dev)
+            torch.cuda.synchronize()
+            g_ref = OS.unscale(OS.average(OS.reduce_slices(sl, w.grad_dtype), w.world),
+                               1.0 / w.loss_scale)
+            g_gpu = rig.g.cpu().numpy()
+            assert np.array_equal(g_gpu.view(np.uint32), g_ref.view(np.uint32)), "stash g"
+            q_gpu = float(rig.sumsq.item())
+            q_ref = OS.sumsq(g_ref)
+            assert abs(q_gpu - q_ref) <= 1e-9 * q_ref, (q_gpu, q_ref)
+            c_gpu = F(rig.clip.item())
+            c_ref = OS.clip_coefficient(q_ref, w.max_norm)
+            assert abs(int(c_gpu.view(np.int32)) - int(c_ref.view(np.int32))) <= 1
+            assert c_gpu == OS.clip_coefficient(q_gpu, w.max_norm)
+            rig.stash_step(cur, t + 1)
+            res = OS.shard_step(sl, w.grad_dtype, w.param_dtype, w.world, p, m, v,
+                                max_norm=w.max_norm, clip_override=c_gpu, **kw)
+            out = cur
+        else:
+            rig.fused(sl_dev, cur, nxt, t + 1)
+            res = OS.shard_step(sl, w.grad_dtype, w.param_dtype, w.world, p, m, v, **kw)
+            out = cur if res.flag else nxt
+        torch.cuda.synchronize()
+        flag = int(rig.flag.item())
+        assert flag == int(res.flag), f"step {step}: flag {flag} vs oracle {res.flag}"
+        gp, gm, gv = (x.cpu().numpy() for x in out)
+        g_used = res.g if w.max_norm <= 0 else np.multiply(res.g, res.clip, dtype=F)
+        n, tot = compare_step(gp, gm, gv, res, p, m, v, g_used,
+                              OS.adam_consts(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t + 1),
+                              f"{w.name} step {step}")
+        same, total = same + n, total + tot
+        # gather buffer: this rank's pieces hold the new params, everything else untouched
+        OS.write_gather(gather_ref, rig.lay.segments, res.params)
+        got = rig.gather_np()
+        mask = rig.slot_mask()
+        assert np.array_equal(got[~mask].view(np.uint32 if got.dtype == F else np.uint16),
+                              gather_ref[~mask].view(np.uint32 if got.dtype == F else np.uint16)), \
+            "write outside the rank's slots"
+        check_params(got[mask], gather_ref[mask], w.param_dtype, f"{w.name} step {step} params")
+        if not res.flag:
+            p, m, v = res.master, res.m, res.v
+            t += 1
+            if w.max_norm <= 0:
+                cur, nxt = nxt, cur
+    say(f"  bitwise-equal state elements: {same}/{total}")
+    assert same == total, f"{total - same} state elements differ in the last bit"
+    return rig
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_small_workloads(name):
+    run_workload(W.SMALL[name])
+
+
+def test_toy_all_ranks_union_equals_unsharded():
+    """Every rank of the toy stepped on the GPU; the gathered parameters equal the
+    oracle's single step over the whole padded vector."""
+    w = W.TOY
+    pl = OP.make_plan(W.numels(w.tensors), w.world)
+    NS = pl.padded_numel
+    gather = np.zeros(NS, F)
+    full_slices = [np.zeros(NS, F) for _ in range(w.world)]
+    full_master = np.zeros(NS, F)
+    for r in range(w.world):
+        rig = Rig(w, rank=r)
+        sl_cpu, sl_dev = rig.slices(1)
+        rig.fused(sl_dev, rig.A, rig.B, 1)
+        torch.cuda.synchronize()
+        assert rig.flag.item() == 0
+        got = rig.gather_np()
+        for goff, _lo, ln, _v in rig.lay.segments:
+            gather[goff:goff + ln] = got[goff:goff + ln]
+            for k in range(w.world):
+                full_slices[k][goff:goff + ln] = sl_cpu[k, :ln].numpy()
+            full_master[goff:goff + ln] = rig.p0
+    one = OS.shard_step(full_slices, "f32", "f32", w.world, full_master, np.zeros(NS, F),
+                        np.zeros(NS, F), lr=w.lr, t=1)
+    assert np.array_equal(gather.view(np.uint32), one.params.view(np.uint32))
+    assert np.all(gather[pl.psi:].view(np.uint32) == 0)
+
+
+def _flat(psi, world, rank, g, p, seed=3, **kw):
+    return W.Workload(name=f"flat{psi}_n{world}_r{rank}_{g}_{p}", tensors=(("x", (psi,)),),
+                      world=world, rank=rank, bucket_cap=0, grad_dtype=g, param_dtype=p,
+                      lr=1e-3, weight_decay=0.05, steps=2, seed=seed, **kw)
+
+
+@pytest.mark.parametrize("g", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("p", ["f32", "bf16", "f16"])
+def test_dtype_matrix(g, p):
+    run_workload(_flat(4 * 5003, 4, 3, g, p))
+
+
+@pytest.mark.parametrize("world,rank,psi", [
+    (1, 0, 12_347),          # N = 1: the whole vector
+    (2, 1, 40_000),          # slot offset 0 mod 16 bytes
+    (3, 2, 30_001),          # N not a power of two: a true IEEE division
+    (8, 1, 8 * 5004),        # bf16 slot 8 mod 16
+    (8, 2, 8 * 5003),        # bf16 slot 4 mod 16 (2 * 10006 = 20012)
+    (8, 1, 8 * 5003 - 5),    # bf16 slot 2 mod 16 and padding at the end of rank 7
+    (16, 15, 16 * 2049 - 9), # padding inside the last rank's shard
+    (64, 63, 750_000),       # many slices
+    (5, 4, 3),               # fewer elements than ranks: this rank is all padding
+])
+def test_world_and_alignment(world, rank, psi):
+    run_workload(_flat(psi, world, rank, "bf16", "bf16"))
+
+
+def test_loss_scaled_fp16():
+    run_workload(_flat(64 * 3001, 64, 63, "f16", "f16", loss_scale=65536.0, grad_zero_frac=0.01))
+
+
+def test_minimal_slice_stride():
+    """Slices packed with the smallest 16-byte-aligned stride (S = 4093, ld = 4096)."""
+    run_workload(_flat(4 * 4093, 4, 1, "bf16", "bf16"), ld_align=8)
+
+
+def test_many_buckets_several_launches():
+    """More pieces than one launch addresses (multi-launch path)."""
+    sizes = [(i * 37) % 211 + 5 for i in range(140)]
+    w = W.Workload(name="many_buckets", tensors=tuple((f"t{i}", (n,)) for i, n in enumerate(sizes)),
+                   world=3, rank=2, bucket_cap=150, grad_dtype="bf16", param_dtype="bf16",
+                   lr=1e-3, weight_decay=0.1, steps=2, seed=9)
+    pl = OP.make_plan(sizes, 3, 150)
+    assert len(pl.buckets) > 60
+    run_workload(w)
+    run_workload(dataclasses.replace(w, max_norm=1e-3, name="many_buckets_clip"))
+
+
+@pytest.mark.parametrize("bad", ["+inf", "-inf", "nan", "f16_overflow"])
+@pytest.mark.parametrize("mode", ["fused", "stash"])
+def test_overflow_skips_bitwise(bad, mode):
+    gk = "f16" if bad == "f16_overflow" else "bf16"
+    w = _flat(8 * 3001, 8, 5, gk, gk, max_norm=(1.0 if mode == "stash" else 0.0))
+    rig = Rig(w)
+    say(f"overflow {bad} {mode}")
+    sl_cpu, _ = rig.slices(1)
+    val = {"+inf": float("inf"), "-inf": float("-inf"), "nan": float("nan"),
+           "f16_overflow": 65520.0}[bad]
+    sl_cpu[6, 1234] = torch.tensor(val).to(sl_cpu.dtype)
+    sl_dev = sl_cpu.to("cuda")
+    before = [x.clone() for x in rig.A]
+    if mode == "fused":
+        rig.B[0].fill_(7.0)
+        rig.fused(sl_dev, rig.A, rig.B, 1)
+    else:
+        rig.reduce_norm(sl_dev)
+        rig.stash_step(rig.A, 1)
+    torch.cuda.synchronize()
+    assert rig.flag.item() == 1
+    for a, b in zip(rig.A, before):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert np.array_equal(rig.gather_np(), rig.gather0)
+
+
+@pytest.mark.parametrize("mode", ["fused", "stash"])
+def test_forced_skip(mode):
+    w = _flat(4 * 2000, 4, 2, "bf16", "bf16", max_norm=(1.0 if mode == "stash" else 0.0))
+    rig = Rig(w)
+    _, sl_dev = rig.slices(1)
+    skip = torch.ones(1, dtype=torch.int32, device="cuda")
+    before = [x.clone() for x in rig.A]
+    if mode == "fused":
+        rig.B[1].fill_(3.0)
+        rig.fused(sl_dev, rig.A, rig.B, 1, skip=skip.data_ptr())
+        torch.cuda.synchronize()
+        assert rig.flag.item() == 1
+        assert torch.all(rig.B[1] == 3.0)
+    else:
+        rig.reduce_norm(sl_dev)
+        a = Z.adam_args(g_stash=rig.g.data_ptr(), clip_coef=rig.clip.data_ptr(),
+                        master_in=rig.A[0].data_ptr(), m_in=rig.A[1].data_ptr(),
+                        v_in=rig.A[2].data_ptr(), master_out=rig.A[0].data_ptr(),
+                        m_out=rig.A[1].data_ptr(), v_out=rig.A[2].data_ptr(),
+                        skip_in=skip.data_ptr(), **rig.common(1))
+        Z.zero_adam_step(rig.plan, a, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+    for a, b in zip(rig.A, before):
+        assert torch.equal(a, b)
+    assert np.array_equal(rig.gather_np(), rig.gather0)
+
+
+def test_no_flag_in_place_matches():
+    """Fused step without an overflow flag, updated in place."""
+    w = _flat(4 * 3000 + 3, 4, 3, "bf16", "bf16")
+    rig = Rig(w)
+    sl_cpu, sl_dev = rig.slices(1)
+    rig.fused(sl_dev, rig.A, rig.A, 1, overflow=False)
+    torch.cuda.synchronize()
+    res = OS.shard_step([storage(sl_cpu[k, :rig.S]) for k in range(4)], "bf16", "bf16", 4,
+                        rig.p0, rig.m0, rig.v0, lr=w.lr, weight_decay=w.weight_decay, t=1)
+    assert np.array_equal(rig.A[0].cpu().numpy().view(np.uint32), res.master.view(np.uint32))
+
+
+def test_norm_deterministic_and_partitioned():
+    w = _flat(16 * 200_003, 16, 7, "bf16", "bf16", max_norm=1.0)
+    rig = Rig(w)
+    _, sl_dev = rig.slices(1)
+    bits = set()
+    for _ in range(10):
+        rig.reduce_norm(sl_dev)
+        torch.cuda.synchronize()
+        bits.add(rig.sumsq.cpu().numpy().view(np.uint64)[0])
+        assert rig.flag.item() == 0
+    assert len(bits) == 1
+    # other ranks' share enters the norm: sqrt(q + other) decides the coefficient
+    q = float(rig.sumsq.item())
+    rig.reduce_norm(sl_dev, other=3 * q, max_norm=1e-3)
+    torch.cuda.synchronize()
+    want = F(1e-3 / np.sqrt(np.float64(q) + 3 * q))
+    assert F(rig.clip.item()) == want
+    rig.reduce_norm(sl_dev, max_norm=1e6)
+    torch.cuda.synchronize()
+    assert rig.clip.item() == 1.0

@@ -1,0 +1,20 @@
+"""One rank's sharded mixed-precision Adam/AdamW step (ZeRO-DP P_os / P_os+g) on MI355X.
+
+The computation runs in libzero_shard.so (hand-written HIP kernels for gfx950
+behind a C ABI, include/zero_shard.h); this package is its thin Python binding
+plus a small optimizer object over torch device tensors.  Importing it loads the
+library and fails loudly if it has not been built.
+"""
+from ._abi import (DTYPE_BYTES, DTYPE_CODES, EXPORTS, ZERO_BF16, ZERO_EALIGN, ZERO_EHIP,
+                   ZERO_EINVAL, ZERO_ENOMEM, ZERO_F16, ZERO_F32, ZERO_OK, Plan, ZeroError,
+                   adam_args, lib, zero_adam_args_t, zero_adam_step, zero_last_error,
+                   zero_reduce_shard, zero_shard_norm, zero_version)
+
+lib()
+
+__all__ = [
+    "DTYPE_BYTES", "DTYPE_CODES", "EXPORTS", "ZERO_BF16", "ZERO_EALIGN", "ZERO_EHIP", "ZERO_EINVAL",
+    "ZERO_ENOMEM", "ZERO_F16", "ZERO_F32", "ZERO_OK", "Plan", "ZeroError", "adam_args", "lib",
+    "zero_adam_args_t", "zero_adam_step", "zero_last_error", "zero_reduce_shard",
+    "zero_shard_norm", "zero_version",
+]

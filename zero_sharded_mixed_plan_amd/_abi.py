@@ -1,0 +1,242 @@
+"""ctypes binding of libzero_shard.so: the C ABI declared in include/zero_shard.h.
+
+Argument marshalling only; every step of the computation runs in the library.
+Functions keep the C names.  Device pointers are plain integers (e.g. a torch
+tensor's data_ptr()); `stream` is a hipStream_t as an integer (0 = null stream).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Tuple
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzero_shard.so")
+
+ZERO_OK, ZERO_EINVAL, ZERO_EALIGN, ZERO_ENOMEM, ZERO_EHIP = 0, -1, -2, -3, -4
+ZERO_F32, ZERO_BF16, ZERO_F16 = 0, 1, 2
+DTYPE_CODES = {"f32": ZERO_F32, "bf16": ZERO_BF16, "f16": ZERO_F16}
+DTYPE_BYTES = {ZERO_F32: 4, ZERO_BF16: 2, ZERO_F16: 2}
+
+# every symbol the header declares
+EXPORTS = [
+    "zero_plan", "zero_plan_free", "zero_plan_shard_numel", "zero_plan_total_numel",
+    "zero_plan_padded_numel", "zero_plan_world", "zero_plan_num_buckets", "zero_plan_num_tensors",
+    "zero_plan_bucket", "zero_plan_tensor", "zero_plan_rank_segment", "zero_plan_bytes",
+    "zero_workspace_bytes", "zero_reduce_shard", "zero_shard_norm", "zero_adam_step",
+    "zero_last_error", "zero_version",
+]
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class zero_adam_args_t(ctypes.Structure):
+    _fields_ = [
+        ("rank", ctypes.c_int32),
+        ("grad", ctypes.c_void_p),
+        ("grad_ld", ctypes.c_int64),
+        ("grad_dtype", ctypes.c_int),
+        ("inv_scale", ctypes.c_float),
+        ("g_stash", ctypes.c_void_p),
+        ("clip_coef", ctypes.c_void_p),
+        ("master_in", ctypes.c_void_p),
+        ("m_in", ctypes.c_void_p),
+        ("v_in", ctypes.c_void_p),
+        ("master_out", ctypes.c_void_p),
+        ("m_out", ctypes.c_void_p),
+        ("v_out", ctypes.c_void_p),
+        ("gather", ctypes.c_void_p),
+        ("param_dtype", ctypes.c_int),
+        ("lr", ctypes.c_double),
+        ("beta1", ctypes.c_double),
+        ("beta2", ctypes.c_double),
+        ("eps", ctypes.c_double),
+        ("weight_decay", ctypes.c_double),
+        ("step", ctypes.c_int64),
+        ("skip_in", ctypes.c_void_p),
+        ("overflow_out", ctypes.c_void_p),
+        ("ev_begin", ctypes.c_void_p),
+        ("ev_end", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once.  Fails loudly when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    # torch first: the library must bind to the HIP runtime torch already uses
+    # for the device memory and streams it hands over (one runtime per process)
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m zero_sharded_mixed_plan_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, f32, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_double
+    P64, P32 = ctypes.POINTER(i64), ctypes.POINTER(i32)
+    sig = {
+        "zero_plan": (ctypes.c_int, [P64, i32, i32, i64, ctypes.POINTER(vp)]),
+        "zero_plan_free": (None, [vp]),
+        "zero_plan_shard_numel": (i64, [vp]),
+        "zero_plan_total_numel": (i64, [vp]),
+        "zero_plan_padded_numel": (i64, [vp]),
+        "zero_plan_world": (i32, [vp]),
+        "zero_plan_num_buckets": (i32, [vp]),
+        "zero_plan_num_tensors": (i32, [vp]),
+        "zero_plan_bucket": (ctypes.c_int, [vp, i32, P64, P64, P64, P64, P32, P32]),
+        "zero_plan_tensor": (ctypes.c_int, [vp, i32, P32, P64]),
+        "zero_plan_rank_segment": (ctypes.c_int, [vp, i32, i32, P64, P64, P64]),
+        "zero_plan_bytes": (ctypes.c_int, [vp, i32, ctypes.POINTER(f64), P64]),
+        "zero_workspace_bytes": (ctypes.c_size_t, [vp]),
+        "zero_reduce_shard": (ctypes.c_int, [vp, vp, i64, ctypes.c_int, f32, vp, vp, i32, vp]),
+        "zero_shard_norm": (ctypes.c_int, [vp, vp, f64, f32, vp, vp, vp, vp]),
+        "zero_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(zero_adam_args_t), vp]),
+        "zero_last_error": (ctypes.c_char_p, []),
+        "zero_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(rc: int) -> None:
+    if rc != ZERO_OK:
+        raise ZeroError(rc, lib().zero_last_error().decode())
+
+
+def zero_last_error() -> str:
+    return lib().zero_last_error().decode()
+
+
+def zero_version() -> str:
+    return lib().zero_version().decode()
+
+
+# ---------------------------------------------------------------------------
+# planner
+# ---------------------------------------------------------------------------
+
+class Plan:
+    """Owner of a zero_plan_t handle."""
+
+    def __init__(self, numels, world: int, bucket_cap: int = 0):
+        L = lib()
+        arr = (ctypes.c_int64 * len(numels))(*[int(n) for n in numels])
+        h = ctypes.c_void_p()
+        _check(L.zero_plan(arr, len(numels), int(world), int(bucket_cap), ctypes.byref(h)))
+        self._h = h
+        self.world = int(world)
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._h is None:
+            raise ValueError("plan already freed")
+        return self._h
+
+    def free(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            lib().zero_plan_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+    @property
+    def shard_numel(self) -> int:
+        return lib().zero_plan_shard_numel(self.handle)
+
+    @property
+    def total_numel(self) -> int:
+        return lib().zero_plan_total_numel(self.handle)
+
+    @property
+    def padded_numel(self) -> int:
+        return lib().zero_plan_padded_numel(self.handle)
+
+    @property
+    def num_buckets(self) -> int:
+        return lib().zero_plan_num_buckets(self.handle)
+
+    @property
+    def num_tensors(self) -> int:
+        return lib().zero_plan_num_tensors(self.handle)
+
+    def bucket(self, b: int) -> Tuple[int, int, int, int, int, int]:
+        """(base, numel, padded, shard, first_tensor, n_tensors)"""
+        o = [ctypes.c_int64() for _ in range(4)] + [ctypes.c_int32() for _ in range(2)]
+        _check(lib().zero_plan_bucket(self.handle, b, *[ctypes.byref(x) for x in o]))
+        return tuple(x.value for x in o)
+
+    def tensor(self, i: int) -> Tuple[int, int]:
+        """(bucket, flat offset)"""
+        b, off = ctypes.c_int32(), ctypes.c_int64()
+        _check(lib().zero_plan_tensor(self.handle, i, ctypes.byref(b), ctypes.byref(off)))
+        return b.value, off.value
+
+    def rank_segment(self, rank: int, b: int) -> Tuple[int, int, int]:
+        """(gather_off, local_off, valid)"""
+        o = [ctypes.c_int64() for _ in range(3)]
+        _check(lib().zero_plan_rank_segment(self.handle, rank, b, *[ctypes.byref(x) for x in o]))
+        return tuple(x.value for x in o)
+
+    def segments(self, rank: int) -> List[Tuple[int, int, int, int]]:
+        """(gather_off, local_off, seg_len, valid) per bucket."""
+        out = []
+        for b in range(self.num_buckets):
+            go, lo, valid = self.rank_segment(rank, b)
+            out.append((go, lo, self.bucket(b)[3], valid))
+        return out
+
+    def tensor_offsets(self) -> List[int]:
+        return [self.tensor(i)[1] for i in range(self.num_tensors)]
+
+    def bytes(self, stage: int) -> Tuple[float, int]:
+        f, p = ctypes.c_double(), ctypes.c_int64()
+        _check(lib().zero_plan_bytes(self.handle, stage, ctypes.byref(f), ctypes.byref(p)))
+        return f.value, p.value
+
+    def workspace_bytes(self) -> int:
+        return lib().zero_workspace_bytes(self.handle)
+
+
+# ---------------------------------------------------------------------------
+# device operations
+# ---------------------------------------------------------------------------
+
+def zero_reduce_shard(plan: Plan, grad: int, grad_ld: int, grad_dtype: int, inv_scale: float,
+                      g_out: int, ws: int, want_sumsq: bool, stream: int = 0) -> None:
+    _check(lib().zero_reduce_shard(plan.handle, grad, grad_ld, grad_dtype, inv_scale, g_out or None,
+                                   ws, 1 if want_sumsq else 0, stream or None))
+
+
+def zero_shard_norm(plan: Plan, ws: int, other_ranks_sumsq: float, max_norm: float,
+                    overflow_out: int, sumsq_out: int, clip_coef_out: int, stream: int = 0) -> None:
+    _check(lib().zero_shard_norm(plan.handle, ws, other_ranks_sumsq, max_norm, overflow_out or None,
+                                 sumsq_out or None, clip_coef_out or None, stream or None))
+
+
+def zero_adam_step(plan: Plan, args: zero_adam_args_t, stream: int = 0) -> None:
+    _check(lib().zero_adam_step(plan.handle, ctypes.byref(args), stream or None))
+
+
+def adam_args(**kw) -> zero_adam_args_t:
+    """Build a zero_adam_args_t; unspecified pointers are NULL, inv_scale 1."""
+    a = zero_adam_args_t()
+    a.inv_scale = 1.0
+    for k, v in kw.items():
+        if not hasattr(a, k):
+            raise TypeError(f"unknown field {k}")
+        setattr(a, k, v)
+    return a

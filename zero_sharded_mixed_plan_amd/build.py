@@ -1,0 +1,57 @@
+"""Build libzero_shard.so (HIP kernels for gfx950 + C++ planner + C ABI) in-tree.
+
+    python -m zero_sharded_mixed_plan_amd.build
+
+The library is loaded into processes that already hold torch's HIP runtime
+(torch supplies the device memory and streams), so the code object version is
+pinned to one every ROCm 7 runtime loads.
+
+Floating-point flags are part of the contract of the library: no contraction
+into fused multiply-add, IEEE-correct fp32 division and square root, denormals
+kept.  Packed-fp32 instructions are disabled for the device code.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB = os.path.join(PKG, "libzero_shard.so")
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("kernels.hip", "abi.cpp", "plan.cpp")]
+ARCH = "gfx950"
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fno-fast-math",
+    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(p):
+        raise RuntimeError("hipcc not found")
+    return p
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library; returns its path.  Always recompiles."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
+           "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,294 @@
+// C ABI of the device operations: argument validation (before anything is
+// enqueued), fp32 step constants, and the launch sequence of each call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "zero_internal.h"
+
+namespace zk {
+
+static thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+}  // namespace zk
+
+using zk::fail;
+
+extern "C" const char* zero_last_error(void) { return zk::g_err.c_str(); }
+extern "C" const char* zero_version(void) { return "zero_shard 0.1 (gfx950)"; }
+
+namespace {
+
+int dtype_bytes(zero_dtype_t t) {
+  switch (t) {
+    case ZERO_F32: return 4;
+    case ZERO_BF16: return 2;
+    case ZERO_F16: return 2;
+  }
+  return 0;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+  const char* name;
+};
+
+bool overlaps(const Range& x, const Range& y) { return x.lo < y.hi && y.lo < x.hi; }
+
+Range rng(const void* p, int64_t bytes, const char* name) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + (uintptr_t)bytes, name};
+}
+
+// Slice dtype/stride checks shared by the fused step and the reduce pass.
+int check_slices(const char* fn, const void* grad, int64_t ld, zero_dtype_t gt, int64_t S) {
+  const int gb = dtype_bytes(gt);
+  if (gb == 0) return fail(ZERO_EINVAL, std::string(fn) + ": unsupported gradient dtype");
+  if (!grad) return fail(ZERO_EINVAL, std::string(fn) + ": grad is NULL");
+  if (ld < S) return fail(ZERO_EINVAL, std::string(fn) + ": grad_ld is smaller than the shard");
+  if (!aligned(grad, 16) || (ld * gb) % 16 != 0)
+    return fail(ZERO_EALIGN, std::string(fn) + ": slices must start on 16-byte boundaries");
+  return ZERO_OK;
+}
+
+void slice_consts(int32_t n, int32_t* n_pow2, float* nf, float* recip) {
+  *n_pow2 = (n & (n - 1)) == 0 ? 1 : 0;
+  *nf = (float)n;
+  *recip = (float)(1.0 / (double)n);
+}
+
+int reduce_grid(int64_t S) {
+  const int64_t nvec = (S + zk::kVec - 1) / zk::kVec;
+  const int64_t b = (nvec + zk::kThreads - 1) / zk::kThreads;
+  return (int)(b < zk::kReduceBlocks ? b : zk::kReduceBlocks);
+}
+
+}  // namespace
+
+extern "C" int zero_reduce_shard(const zero_plan_t* plan, const void* grad, int64_t grad_ld,
+                                 zero_dtype_t grad_dtype, float inv_scale, float* g_out, void* ws,
+                                 int32_t want_sumsq, void* stream) {
+  if (!plan) return fail(ZERO_EINVAL, "zero_reduce_shard: plan is NULL");
+  if (!ws) return fail(ZERO_EINVAL, "zero_reduce_shard: workspace is NULL");
+  if (!aligned(ws, 16)) return fail(ZERO_EALIGN, "zero_reduce_shard: workspace must be 16-byte aligned");
+  const int64_t S = plan->shard;
+  int rc = check_slices("zero_reduce_shard", grad, grad_ld, grad_dtype, S);
+  if (rc) return rc;
+  if (g_out && !aligned(g_out, 16)) return fail(ZERO_EALIGN, "zero_reduce_shard: g_out must be 16-byte aligned");
+  if (!std::isfinite(inv_scale)) return fail(ZERO_EINVAL, "zero_reduce_shard: inv_scale is not finite");
+  if (g_out) {
+    const int gb = dtype_bytes(grad_dtype);
+    const Range gr = rng(grad, ((int64_t)(plan->world - 1) * grad_ld + S) * gb, "grad");
+    if (overlaps(gr, rng(g_out, S * 4, "g_out")))
+      return fail(ZERO_EINVAL, "zero_reduce_shard: g_out overlaps the slices");
+  }
+  zk::ReduceLaunch a{};
+  a.grad = grad;
+  a.ld_bytes = grad_ld * dtype_bytes(grad_dtype);
+  a.n = plan->world;
+  slice_consts(a.n, &a.n_pow2, &a.nf, &a.recip_n);
+  a.inv_scale = inv_scale;
+  a.g_out = g_out;
+  a.ws_flags = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + zk::ws_flags_offset());
+  a.ws_sums = reinterpret_cast<double*>(static_cast<char*>(ws) + zk::ws_sums_offset());
+  a.want_sumsq = want_sumsq ? 1 : 0;
+  a.S = S;
+  a.nvec = (S + zk::kVec - 1) / zk::kVec;
+  return zk::launch_reduce(a, grad_dtype, reduce_grid(S), stream);
+}
+
+extern "C" int zero_shard_norm(const zero_plan_t* plan, const void* ws, double other_ranks_sumsq,
+                               float max_norm, uint32_t* overflow_out, double* sumsq_out,
+                               float* clip_coef_out, void* stream) {
+  if (!plan) return fail(ZERO_EINVAL, "zero_shard_norm: plan is NULL");
+  if (!ws) return fail(ZERO_EINVAL, "zero_shard_norm: workspace is NULL");
+  if (!aligned(ws, 16)) return fail(ZERO_EALIGN, "zero_shard_norm: workspace must be 16-byte aligned");
+  if (!std::isfinite(other_ranks_sumsq) || other_ranks_sumsq < 0)
+    return fail(ZERO_EINVAL, "zero_shard_norm: other_ranks_sumsq must be finite and >= 0");
+  if (!std::isfinite(max_norm)) return fail(ZERO_EINVAL, "zero_shard_norm: max_norm is not finite");
+  if ((sumsq_out && !aligned(sumsq_out, 8)) || (clip_coef_out && !aligned(clip_coef_out, 4)) ||
+      (overflow_out && !aligned(overflow_out, 4)))
+    return fail(ZERO_EALIGN, "zero_shard_norm: misaligned output");
+  zk::NormLaunch a{};
+  a.ws_flags = reinterpret_cast<const uint32_t*>(static_cast<const char*>(ws) + zk::ws_flags_offset());
+  a.ws_sums = reinterpret_cast<const double*>(static_cast<const char*>(ws) + zk::ws_sums_offset());
+  a.nblocks = reduce_grid(plan->shard);
+  a.other_sumsq = other_ranks_sumsq;
+  a.max_norm = (double)max_norm;
+  a.overflow_out = overflow_out;
+  a.sumsq_out = sumsq_out;
+  a.clip_out = clip_coef_out;
+  return zk::launch_norm(a, stream);
+}
+
+extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* args, void* stream) {
+  if (!plan) return fail(ZERO_EINVAL, "zero_adam_step: plan is NULL");
+  if (!args) return fail(ZERO_EINVAL, "zero_adam_step: args is NULL");
+  const zero_adam_args_t& A = *args;
+  const int64_t S = plan->shard;
+  const int32_t N = plan->world;
+  if (A.rank < 0 || A.rank >= N) return fail(ZERO_EINVAL, "zero_adam_step: rank out of range");
+  const bool stash = A.g_stash != nullptr;
+  const int pb = dtype_bytes(A.param_dtype);
+  if (pb == 0) return fail(ZERO_EINVAL, "zero_adam_step: unsupported parameter dtype");
+
+  // pointers and alignment
+  const float* ins[3] = {A.master_in, A.m_in, A.v_in};
+  float* outs[3] = {A.master_out, A.m_out, A.v_out};
+  for (int i = 0; i < 3; ++i) {
+    if (!ins[i] || !outs[i]) return fail(ZERO_EINVAL, "zero_adam_step: state pointer is NULL");
+    if (!aligned(ins[i], 16) || !aligned(outs[i], 16))
+      return fail(ZERO_EALIGN, "zero_adam_step: state arrays must be 16-byte aligned");
+  }
+  if (!A.gather) return fail(ZERO_EINVAL, "zero_adam_step: gather is NULL");
+  if (!aligned(A.gather, pb)) return fail(ZERO_EALIGN, "zero_adam_step: gather is not element aligned");
+  if (stash) {
+    if (!aligned(A.g_stash, 16)) return fail(ZERO_EALIGN, "zero_adam_step: g_stash must be 16-byte aligned");
+    if (A.clip_coef && !aligned(A.clip_coef, 4)) return fail(ZERO_EALIGN, "zero_adam_step: clip_coef misaligned");
+  } else {
+    const int rc = check_slices("zero_adam_step", A.grad, A.grad_ld, A.grad_dtype, S);
+    if (rc) return rc;
+    if (!std::isfinite(A.inv_scale)) return fail(ZERO_EINVAL, "zero_adam_step: inv_scale is not finite");
+  }
+  if ((A.skip_in && !aligned(A.skip_in, 4)) || (A.overflow_out && !aligned(A.overflow_out, 4)))
+    return fail(ZERO_EALIGN, "zero_adam_step: flag pointers must be 4-byte aligned");
+
+  // hyper-parameters
+  if (!(std::isfinite(A.lr) && A.lr >= 0) || !(A.beta1 >= 0 && A.beta1 < 1) ||
+      !(A.beta2 >= 0 && A.beta2 < 1) || !(std::isfinite(A.eps) && A.eps >= 0) ||
+      !std::isfinite(A.weight_decay))
+    return fail(ZERO_EINVAL, "zero_adam_step: bad hyper-parameters");
+  if (A.step < 1) return fail(ZERO_EINVAL, "zero_adam_step: step counts from 1");
+
+  // aliasing: outputs never overlap each other or the gather buffer; in the
+  // fused step with an overflow flag they must not overlap any input either
+  // (the inputs are what a skipped step keeps)
+  const int64_t sb = S * 4;
+  std::vector<Range> out_r = {rng(A.master_out, sb, "master_out"), rng(A.m_out, sb, "m_out"),
+                              rng(A.v_out, sb, "v_out"),
+                              rng(A.gather, plan->padded * pb, "gather")};
+  for (size_t i = 0; i < out_r.size(); ++i)
+    for (size_t j = i + 1; j < out_r.size(); ++j)
+      if (overlaps(out_r[i], out_r[j]))
+        return fail(ZERO_EINVAL, std::string("zero_adam_step: ") + out_r[i].name + " overlaps " + out_r[j].name);
+  std::vector<Range> in_r = {rng(A.master_in, sb, "master_in"), rng(A.m_in, sb, "m_in"),
+                             rng(A.v_in, sb, "v_in")};
+  if (stash)
+    in_r.push_back(rng(A.g_stash, sb, "g_stash"));
+  else
+    in_r.push_back(rng(A.grad, ((int64_t)(N - 1) * A.grad_ld + S) * dtype_bytes(A.grad_dtype), "grad"));
+  const bool strict = !stash && A.overflow_out != nullptr;
+  for (size_t i = 0; i < in_r.size(); ++i) {
+    for (size_t j = 0; j < out_r.size(); ++j) {
+      if (!overlaps(in_r[i], out_r[j])) continue;
+      const bool same = (i < 3 && j == i && in_r[i].lo == out_r[j].lo);  // exact in-place update
+      if (strict || !same)
+        return fail(ZERO_EINVAL, std::string("zero_adam_step: ") + in_r[i].name + " overlaps " + out_r[j].name +
+                                     (strict ? " (a fused step with an overflow flag needs separate output state)" : ""));
+    }
+  }
+
+  // fp32 constants, rounded once from float64
+  zk::StepLaunch L{};
+  L.c.b1 = (float)A.beta1;
+  L.c.b2 = (float)A.beta2;
+  L.c.omb1 = (float)(1.0 - A.beta1);
+  L.c.omb2 = (float)(1.0 - A.beta2);
+  L.c.bc1 = (float)(1.0 - std::pow(A.beta1, (double)A.step));
+  L.c.bc2 = (float)(1.0 - std::pow(A.beta2, (double)A.step));
+  L.c.lr = (float)A.lr;
+  L.c.eps = (float)A.eps;
+  L.c.dec = (float)(1.0 - A.lr * A.weight_decay);
+  if (!(L.c.bc1 > 0.0f) || !(L.c.bc2 > 0.0f))
+    return fail(ZERO_EINVAL, "zero_adam_step: bias correction rounds to 0 in fp32");
+
+  L.grad = A.grad;
+  L.ld_bytes = stash ? 0 : A.grad_ld * dtype_bytes(A.grad_dtype);
+  L.n = N;
+  slice_consts(N, &L.n_pow2, &L.nf, &L.recip_n);
+  L.inv_scale = A.inv_scale;
+  L.g_stash = A.g_stash;
+  L.clip = A.clip_coef;
+  L.p_in = A.master_in;
+  L.m_in = A.m_in;
+  L.v_in = A.v_in;
+  L.p_out = A.master_out;
+  L.m_out = A.m_out;
+  L.v_out = A.v_out;
+  L.gather = static_cast<char*>(A.gather);
+  L.skip_in = A.skip_in;
+  L.overflow = stash ? nullptr : A.overflow_out;
+  L.S = S;
+
+  // Split the rank's pieces into launches of at most kMaxSeg pieces.  A launch
+  // covers whole 8-element vectors; the vector holding a piece boundary goes to
+  // the launch that lists both pieces.
+  const int nb = (int)plan->buckets.size();
+  struct Group { int64_t v_lo, v_hi; int first, count; };
+  std::vector<Group> groups;
+  const int64_t nvec = (S + zk::kVec - 1) / zk::kVec;
+  {
+    int first = 0;
+    int64_t v_lo = 0;
+    while (first < nb) {
+      const int last = first + zk::kMaxSeg < nb ? first + zk::kMaxSeg : nb;  // exclusive
+      int64_t v_hi = nvec;
+      if (last < nb) v_hi = plan->buckets[last].local_off / zk::kVec;
+      groups.push_back(Group{v_lo, v_hi, first, last - first});
+      // the next launch starts with the piece holding element 8*v_hi
+      if (last < nb) {
+        int nf = last;
+        while (nf > first && plan->buckets[nf].local_off > v_hi * zk::kVec) --nf;
+        first = nf;
+      } else {
+        first = nb;
+      }
+      v_lo = v_hi;
+    }
+  }
+
+  int rc = ZERO_OK;
+  if (strict) rc = zk::launch_fill_u32(A.overflow_out, 0u, stream);
+  if (rc) return rc;
+  rc = zk::record_event(A.ev_begin, stream);
+  if (rc) return rc;
+  for (const Group& g : groups) {
+    L.v_lo = g.v_lo;
+    L.v_hi = g.v_hi;
+    L.nseg = g.count;
+    for (int s = 0; s < g.count; ++s) {
+      const auto& B = plan->buckets[g.first + s];
+      L.seg[s].end = B.local_off + B.shard;
+      L.seg[s].delta = (B.base + (int64_t)A.rank * B.shard) - B.local_off;
+    }
+    rc = zk::launch_step(L, A.grad_dtype, A.param_dtype, stash, stream);
+    if (rc) return rc;
+  }
+  rc = zk::record_event(A.ev_end, stream);
+  if (rc) return rc;
+  if (strict) {
+    for (const Group& g : groups) {
+      L.v_lo = g.v_lo;
+      L.v_hi = g.v_hi;
+      L.nseg = g.count;
+      for (int s = 0; s < g.count; ++s) {
+        const auto& B = plan->buckets[g.first + s];
+        L.seg[s].end = B.local_off + B.shard;
+        L.seg[s].delta = (B.base + (int64_t)A.rank * B.shard) - B.local_off;
+      }
+      rc = zk::launch_recast(L, A.param_dtype, A.overflow_out, stream);
+      if (rc) return rc;
+    }
+  }
+  return ZERO_OK;
+}

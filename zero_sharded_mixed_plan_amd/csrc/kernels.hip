@@ -1,0 +1,534 @@
+// HIP kernels for gfx950 (CDNA4): one rank's sharded mixed-precision AdamW step.
+//
+// The step is a pure streaming update (well under one flop per byte), so it is
+// bound by HBM bandwidth, not by the matrix cores: every kernel here is written
+// for wide, coalesced global traffic.  Each thread owns kVec = 8 consecutive
+// elements, so every gradient slice is read with one 16-byte load (two for fp32)
+// and every fp32 state array with two 16-byte loads; a wave64 therefore touches
+// 1 KiB contiguous per 16-bit slice.  All loads of a tile are issued before the
+// arithmetic so enough bytes are in flight to cover HBM latency.
+//
+// What is computed follows zero_adam.py ("ZeRO 与 FSDP：切分优化器状态、梯度与参数",
+// section "从零实现 ZeRO 的 Adam"): SUM of the ranks' gradient pieces, / N, Adam on
+// fp32 master/m/v, then the new parameters go to the all-gather buffer; plus the
+// loss-scale unscale and overflow skip of mixed precision ("PaddlePaddle
+// ZeRO优化…", section "混合精度才是最佳拍档") and decoupled weight decay (AdamW).
+// Arithmetic is IEEE fp32, one rounding per operation: the build disables
+// contraction into FMA, keeps denormals and uses correctly rounded div/sqrt.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+
+#include "zero_internal.h"
+
+namespace zk {
+
+using u32 = uint32_t;
+
+// ---------------------------------------------------------------------------
+// element types
+// ---------------------------------------------------------------------------
+
+struct TF32 { static constexpr int bytes = 4; };
+struct TBF16 { static constexpr int bytes = 2; };
+struct TF16 { static constexpr int bytes = 2; };
+
+// 8 elements of a slice, raw: one uint4 for 16-bit types, two for fp32.
+template <class T>
+struct Raw { uint4 q[T::bytes / 2]; };
+
+template <class T>
+__device__ __forceinline__ Raw<T> ld_raw(const char* p) {
+  Raw<T> r;
+#pragma unroll
+  for (int i = 0; i < T::bytes / 2; ++i) r.q[i] = reinterpret_cast<const uint4*>(p)[i];
+  return r;
+}
+
+__device__ __forceinline__ float bf16_lo(u32 w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(u32 w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_bits(u32 h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+template <class T> __device__ __forceinline__ void widen8(const Raw<T>& r, float o[8]);
+
+template <> __device__ __forceinline__ void widen8<TBF16>(const Raw<TBF16>& r, float o[8]) {
+  const u32 w[4] = {r.q[0].x, r.q[0].y, r.q[0].z, r.q[0].w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { o[2 * i] = bf16_lo(w[i]); o[2 * i + 1] = bf16_hi(w[i]); }
+}
+template <> __device__ __forceinline__ void widen8<TF16>(const Raw<TF16>& r, float o[8]) {
+  const u32 w[4] = {r.q[0].x, r.q[0].y, r.q[0].z, r.q[0].w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { o[2 * i] = f16_bits(w[i] & 0xffffu); o[2 * i + 1] = f16_bits(w[i] >> 16); }
+}
+template <> __device__ __forceinline__ void widen8<TF32>(const Raw<TF32>& r, float o[8]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    o[4 * i + 0] = __uint_as_float(r.q[i].x);
+    o[4 * i + 1] = __uint_as_float(r.q[i].y);
+    o[4 * i + 2] = __uint_as_float(r.q[i].z);
+    o[4 * i + 3] = __uint_as_float(r.q[i].w);
+  }
+}
+
+// one element of a slice, widened
+template <class T> __device__ __forceinline__ float ld_one(const char* p);
+template <> __device__ __forceinline__ float ld_one<TF32>(const char* p) { return *reinterpret_cast<const float*>(p); }
+template <> __device__ __forceinline__ float ld_one<TBF16>(const char* p) {
+  return __uint_as_float((u32)(*reinterpret_cast<const uint16_t*>(p)) << 16);
+}
+template <> __device__ __forceinline__ float ld_one<TF16>(const char* p) {
+  return f16_bits(*reinterpret_cast<const uint16_t*>(p));
+}
+
+// fp32 -> parameter storage, round to nearest even (hardware conversions)
+__device__ __forceinline__ u32 pack_bf16(float a, float b) {
+  const uint16_t x = __builtin_bit_cast(uint16_t, (__bf16)a);
+  const uint16_t y = __builtin_bit_cast(uint16_t, (__bf16)b);
+  return (u32)x | ((u32)y << 16);
+}
+__device__ __forceinline__ u32 pack_f16(float a, float b) {
+  const uint16_t x = __builtin_bit_cast(uint16_t, (_Float16)a);
+  const uint16_t y = __builtin_bit_cast(uint16_t, (_Float16)b);
+  return (u32)x | ((u32)y << 16);
+}
+
+// Store 8 parameters at dst, choosing the widest naturally aligned store the
+// address allows (a rank's gather slot may sit at any element offset).
+template <class PT> __device__ __forceinline__ void store_params8(char* dst, const float p[8]);
+
+template <class PT>
+__device__ __forceinline__ void store_words(char* dst, const u32* w) {
+  constexpr int NW = PT::bytes * 2;  // 4 words for 16-bit, 8 for fp32
+  const uintptr_t a = reinterpret_cast<uintptr_t>(dst);
+  if ((a & 15) == 0) {
+#pragma unroll
+    for (int i = 0; i < NW; i += 4)
+      *reinterpret_cast<uint4*>(dst + 4 * i) = make_uint4(w[i], w[i + 1], w[i + 2], w[i + 3]);
+  } else if ((a & 7) == 0) {
+#pragma unroll
+    for (int i = 0; i < NW; i += 2) *reinterpret_cast<uint2*>(dst + 4 * i) = make_uint2(w[i], w[i + 1]);
+  } else if ((a & 3) == 0) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) *reinterpret_cast<u32*>(dst + 4 * i) = w[i];
+  } else {  // 2-byte aligned 16-bit elements
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      reinterpret_cast<uint16_t*>(dst)[2 * i] = (uint16_t)(w[i] & 0xffffu);
+      reinterpret_cast<uint16_t*>(dst)[2 * i + 1] = (uint16_t)(w[i] >> 16);
+    }
+  }
+}
+template <> __device__ __forceinline__ void store_params8<TBF16>(char* dst, const float p[8]) {
+  const u32 w[4] = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
+  store_words<TBF16>(dst, w);
+}
+template <> __device__ __forceinline__ void store_params8<TF16>(char* dst, const float p[8]) {
+  const u32 w[4] = {pack_f16(p[0], p[1]), pack_f16(p[2], p[3]), pack_f16(p[4], p[5]), pack_f16(p[6], p[7])};
+  store_words<TF16>(dst, w);
+}
+template <> __device__ __forceinline__ void store_params8<TF32>(char* dst, const float p[8]) {
+  u32 w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = __float_as_uint(p[i]);
+  store_words<TF32>(dst, w);
+}
+
+template <class PT> __device__ __forceinline__ void store_param1(char* dst, float p);
+template <> __device__ __forceinline__ void store_param1<TF32>(char* dst, float p) { *reinterpret_cast<float*>(dst) = p; }
+template <> __device__ __forceinline__ void store_param1<TBF16>(char* dst, float p) {
+  *reinterpret_cast<uint16_t*>(dst) = __builtin_bit_cast(uint16_t, (__bf16)p);
+}
+template <> __device__ __forceinline__ void store_param1<TF16>(char* dst, float p) {
+  *reinterpret_cast<uint16_t*>(dst) = __builtin_bit_cast(uint16_t, (_Float16)p);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 state
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void ld8(const float* p, float o[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+__device__ __forceinline__ void st8(float* p, const float o[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(o[0], o[1], o[2], o[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(o[4], o[5], o[6], o[7]);
+}
+
+// ---------------------------------------------------------------------------
+// the arithmetic of one element (shared by all paths of all kernels)
+// ---------------------------------------------------------------------------
+
+// g = (acc / N) * inv_scale: an IEEE quotient; for N a power of two the product
+// with the exact reciprocal is the same correctly rounded value.
+__device__ __forceinline__ float average_unscale(float acc, int n_pow2, float nf, float recip_n,
+                                                 float inv_scale) {
+  const float g = n_pow2 ? acc * recip_n : acc / nf;
+  return g * inv_scale;
+}
+
+__device__ __forceinline__ void adamw1(float& p, float& m, float& v, float g, const AdamK& c) {
+  const float m2 = c.b1 * m + c.omb1 * g;
+  const float v2 = c.b2 * v + c.omb2 * (g * g);
+  const float m_hat = m2 / c.bc1;
+  const float v_hat = v2 / c.bc2;
+  const float den = __builtin_sqrtf(v_hat) + c.eps;
+  const float u = (c.lr * m_hat) / den;
+  p = c.dec * p - u;
+  m = m2;
+  v = v2;
+}
+
+// Sum of N slices for 8 elements: acc = s_0, then acc += s_k in ascending k.
+// Loads go out in batches of NB before their adds so a wave keeps NB * 1 KiB in
+// flight per batch.
+template <class T, int NB>
+__device__ __forceinline__ void reduce8(const char* base, int64_t ld_bytes, int n, float acc[8]) {
+  const Raw<T> r0 = ld_raw<T>(base);
+  int k = 1;
+  for (; k + NB <= n; k += NB) {
+    Raw<T> r[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) r[b] = ld_raw<T>(base + (int64_t)(k + b) * ld_bytes);
+    if (k == 1) widen8<T>(r0, acc);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float w[8];
+      widen8<T>(r[b], w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + w[e];
+    }
+  }
+  if (k == 1) widen8<T>(r0, acc);
+  const int rest = n - k;  // < NB, uniform
+  if (rest > 0) {
+    Raw<T> r[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (b < rest) r[b] = ld_raw<T>(base + (int64_t)(k + b) * ld_bytes);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b < rest) {
+        float w[8];
+        widen8<T>(r[b], w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + w[e];
+      }
+    }
+  }
+}
+
+template <class T>
+__device__ __forceinline__ float reduce1(const char* base, int64_t ld_bytes, int n) {
+  float acc = ld_one<T>(base);
+  for (int k = 1; k < n; ++k) acc = acc + ld_one<T>(base + (int64_t)k * ld_bytes);
+  return acc;
+}
+
+template <class T> struct Batch { static constexpr int value = 8; };
+template <> struct Batch<TF32> { static constexpr int value = 4; };
+
+// gather index offset of local element j (uniform loop over the launch's pieces)
+__device__ __forceinline__ int64_t delta_of(const StepLaunch& a, int64_t j) {
+  int64_t d = a.seg[0].delta;
+  for (int s = 0; s + 1 < a.nseg; ++s)
+    if (j >= a.seg[s].end) d = a.seg[s + 1].delta;
+  return d;
+}
+
+// ---------------------------------------------------------------------------
+// the update kernel (fused: N slices in; stash: fp32 g in)
+// ---------------------------------------------------------------------------
+
+template <class GT, class PT, bool STASH>
+__global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
+  if (a.skip_in != nullptr && *a.skip_in != 0u) {
+    // skipped by the caller: report it like an overflow so the fused step's
+    // caller keeps its current state and the slots get their pre-step values
+    if (!STASH && a.overflow != nullptr && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.overflow, 1u);
+    return;
+  }
+  const int64_t v = a.v_lo + (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (v >= a.v_hi) return;
+  const int64_t j0 = v * kVec;
+  float clip = 1.0f;
+  if (STASH && a.clip != nullptr) clip = *a.clip;
+
+  float p[8], m[8], s[8], g[8];
+  bool bad = false;
+  if (j0 + kVec <= a.S) {
+    ld8(a.p_in + j0, p);
+    ld8(a.m_in + j0, m);
+    ld8(a.v_in + j0, s);
+    if (STASH) {
+      ld8(a.g_stash + j0, g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[e] = g[e] * clip;
+    } else {
+      float acc[8];
+      reduce8<GT, Batch<GT>::value>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes,
+                                    a.n, acc);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, a.inv_scale);
+        bad |= !__builtin_isfinite(g[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) adamw1(p[e], m[e], s[e], g[e], a.c);
+    st8(a.p_out + j0, p);
+    st8(a.m_out + j0, m);
+    st8(a.v_out + j0, s);
+    const int64_t d0 = delta_of(a, j0);
+    if (delta_of(a, j0 + kVec - 1) == d0) {
+      store_params8<PT>(a.gather + (j0 + d0) * PT::bytes, p);
+    } else {  // the 8 elements straddle two gather pieces
+#pragma unroll
+      for (int e = 0; e < 8; ++e) store_param1<PT>(a.gather + (j0 + e + delta_of(a, j0 + e)) * PT::bytes, p[e]);
+    }
+  } else {
+    // the shard's ragged end: fewer than 8 elements, element by element
+    for (int e = 0; e < 8; ++e) {
+      const int64_t j = j0 + e;
+      if (j >= a.S) break;
+      float pe = a.p_in[j], me = a.m_in[j], ve = a.v_in[j], ge;
+      if (STASH) {
+        ge = a.g_stash[j] * clip;
+      } else {
+        const float acc = reduce1<GT>(static_cast<const char*>(a.grad) + j * GT::bytes, a.ld_bytes, a.n);
+        ge = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, a.inv_scale);
+        bad |= !__builtin_isfinite(ge);
+      }
+      adamw1(pe, me, ve, ge, a.c);
+      a.p_out[j] = pe;
+      a.m_out[j] = me;
+      a.v_out[j] = ve;
+      store_param1<PT>(a.gather + (j + delta_of(a, j)) * PT::bytes, pe);
+    }
+  }
+  if (!STASH && a.overflow != nullptr && bad) atomicOr(a.overflow, 1u);
+}
+
+// On a skipped fused step: rewrite the rank's gather pieces from master_in, so
+// they keep the pre-step parameters.  A no-op unless *cond != 0.
+template <class PT>
+__global__ __launch_bounds__(kThreads) void recast_kernel(const StepLaunch a, const u32* cond) {
+  if (*cond == 0u) return;
+  for (int64_t v = a.v_lo + (int64_t)blockIdx.x * kThreads + threadIdx.x; v < a.v_hi;
+       v += (int64_t)gridDim.x * kThreads) {
+    const int64_t j0 = v * kVec;
+    if (j0 + kVec <= a.S) {
+      float p[8];
+      ld8(a.p_in + j0, p);
+      const int64_t d0 = delta_of(a, j0);
+      if (delta_of(a, j0 + kVec - 1) == d0) {
+        store_params8<PT>(a.gather + (j0 + d0) * PT::bytes, p);
+      } else {
+        for (int e = 0; e < 8; ++e) store_param1<PT>(a.gather + (j0 + e + delta_of(a, j0 + e)) * PT::bytes, p[e]);
+      }
+    } else {
+      for (int64_t j = j0; j < a.S; ++j) store_param1<PT>(a.gather + (j + delta_of(a, j)) * PT::bytes, a.p_in[j]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gradient preparation with per-workgroup overflow words and fp64 sums of g^2
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+template <class GT>
+__global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) {
+  double sq = 0.0;
+  bool bad = false;
+  for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < a.nvec;
+       v += (int64_t)gridDim.x * kThreads) {
+    const int64_t j0 = v * kVec;
+    if (j0 + kVec <= a.S) {
+      float acc[8], g[8];
+      reduce8<GT, Batch<GT>::value>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes, a.n, acc);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, a.inv_scale);
+        bad |= !__builtin_isfinite(g[e]);
+      }
+      if (a.g_out != nullptr) st8(a.g_out + j0, g);
+      if (a.want_sumsq) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sq += (double)g[e] * (double)g[e];
+      }
+    } else {
+      for (int64_t j = j0; j < a.S; ++j) {
+        const float acc = reduce1<GT>(static_cast<const char*>(a.grad) + j * GT::bytes, a.ld_bytes, a.n);
+        const float g = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, a.inv_scale);
+        bad |= !__builtin_isfinite(g);
+        if (a.g_out != nullptr) a.g_out[j] = g;
+        if (a.want_sumsq) sq += (double)g * (double)g;
+      }
+    }
+  }
+  // fixed-order workgroup reduction: xor-shuffle within each wave64, then the 4
+  // wave results in index order
+  __shared__ double s_sum[kThreads / 64];
+  __shared__ u32 s_bad[kThreads / 64];
+  sq = wave_sum(sq);
+  const u32 wbad = __any(bad) ? 1u : 0u;
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_sum[wave] = sq;
+    s_bad[wave] = wbad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    u32 f = 0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      t += s_sum[w];
+      f |= s_bad[w];
+    }
+    a.ws_sums[blockIdx.x] = t;
+    a.ws_flags[blockIdx.x] = f;
+  }
+}
+
+// One workgroup: OR of the overflow words, fixed-order sum of the partials,
+// global norm and clip coefficient.
+__global__ __launch_bounds__(kThreads) void norm_kernel(const NormLaunch a) {
+  double s = 0.0;
+  u32 f = 0;
+  for (int i = threadIdx.x; i < a.nblocks; i += kThreads) {
+    s += a.ws_sums[i];
+    f |= a.ws_flags[i];
+  }
+  __shared__ double s_sum[kThreads];
+  __shared__ u32 s_f[kThreads];
+  s_sum[threadIdx.x] = s;
+  s_f[threadIdx.x] = f;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) {
+      s_sum[threadIdx.x] += s_sum[threadIdx.x + w];
+      s_f[threadIdx.x] |= s_f[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double q = s_sum[0];
+    const double norm = __builtin_sqrt(q + a.other_sumsq);
+    const double c = (a.max_norm > 0.0 && norm > a.max_norm) ? a.max_norm / norm : 1.0;
+    if (a.overflow_out) *a.overflow_out = s_f[0] ? 1u : 0u;
+    if (a.sumsq_out) *a.sumsq_out = q;
+    if (a.clip_out) *a.clip_out = (float)c;
+  }
+}
+
+__global__ void fill_u32_kernel(u32* p, u32 value) {
+  if (threadIdx.x == 0) *p = value;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+static int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    char buf[256];
+    snprintf(buf, sizeof buf, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+    return fail(ZERO_EHIP, buf);
+  }
+  return ZERO_OK;
+}
+
+int launch_fill_u32(u32* p, u32 value, void* stream) {
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, p, value);
+  return check_launch("fill");
+}
+
+template <class GT, class PT, bool STASH>
+static void go_step(const StepLaunch& a, unsigned blocks, hipStream_t st) {
+  hipLaunchKernelGGL((step_kernel<GT, PT, STASH>), dim3(blocks), dim3(kThreads), 0, st, a);
+}
+
+template <class GT, bool STASH>
+static int dispatch_pt(const StepLaunch& a, zero_dtype_t pt, unsigned blocks, hipStream_t st) {
+  switch (pt) {
+    case ZERO_F32: go_step<GT, TF32, STASH>(a, blocks, st); return ZERO_OK;
+    case ZERO_BF16: go_step<GT, TBF16, STASH>(a, blocks, st); return ZERO_OK;
+    case ZERO_F16: go_step<GT, TF16, STASH>(a, blocks, st); return ZERO_OK;
+  }
+  return fail(ZERO_EINVAL, "unsupported parameter dtype");
+}
+
+int launch_step(const StepLaunch& a, zero_dtype_t gt, zero_dtype_t pt, bool stash, void* stream) {
+  const int64_t nv = a.v_hi - a.v_lo;
+  if (nv <= 0) return ZERO_OK;
+  const unsigned blocks = (unsigned)((nv + kThreads - 1) / kThreads);
+  hipStream_t st = (hipStream_t)stream;
+  int rc;
+  if (stash) {
+    rc = dispatch_pt<TF32, true>(a, pt, blocks, st);
+  } else {
+    switch (gt) {
+      case ZERO_F32: rc = dispatch_pt<TF32, false>(a, pt, blocks, st); break;
+      case ZERO_BF16: rc = dispatch_pt<TBF16, false>(a, pt, blocks, st); break;
+      case ZERO_F16: rc = dispatch_pt<TF16, false>(a, pt, blocks, st); break;
+      default: return fail(ZERO_EINVAL, "unsupported gradient dtype");
+    }
+  }
+  if (rc != ZERO_OK) return rc;
+  return check_launch("step");
+}
+
+int launch_recast(const StepLaunch& a, zero_dtype_t pt, const u32* cond, void* stream) {
+  const int64_t nv = a.v_hi - a.v_lo;
+  if (nv <= 0) return ZERO_OK;
+  int64_t b = (nv + kThreads - 1) / kThreads;
+  const unsigned blocks = (unsigned)(b < 1024 ? b : 1024);
+  hipStream_t st = (hipStream_t)stream;
+  switch (pt) {
+    case ZERO_F32: hipLaunchKernelGGL(recast_kernel<TF32>, dim3(blocks), dim3(kThreads), 0, st, a, cond); break;
+    case ZERO_BF16: hipLaunchKernelGGL(recast_kernel<TBF16>, dim3(blocks), dim3(kThreads), 0, st, a, cond); break;
+    case ZERO_F16: hipLaunchKernelGGL(recast_kernel<TF16>, dim3(blocks), dim3(kThreads), 0, st, a, cond); break;
+    default: return fail(ZERO_EINVAL, "unsupported parameter dtype");
+  }
+  return check_launch("recast");
+}
+
+int launch_reduce(const ReduceLaunch& a, zero_dtype_t gt, int32_t nblocks, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  switch (gt) {
+    case ZERO_F32: hipLaunchKernelGGL(reduce_kernel<TF32>, dim3(nblocks), dim3(kThreads), 0, st, a); break;
+    case ZERO_BF16: hipLaunchKernelGGL(reduce_kernel<TBF16>, dim3(nblocks), dim3(kThreads), 0, st, a); break;
+    case ZERO_F16: hipLaunchKernelGGL(reduce_kernel<TF16>, dim3(nblocks), dim3(kThreads), 0, st, a); break;
+    default: return fail(ZERO_EINVAL, "unsupported gradient dtype");
+  }
+  return check_launch("reduce");
+}
+
+int launch_norm(const NormLaunch& a, void* stream) {
+  hipLaunchKernelGGL(norm_kernel, dim3(1), dim3(kThreads), 0, (hipStream_t)stream, a);
+  return check_launch("norm");
+}
+
+int record_event(void* ev, void* stream) {
+  if (ev == nullptr) return ZERO_OK;
+  const hipError_t e = hipEventRecord((hipEvent_t)ev, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    char buf[256];
+    snprintf(buf, sizeof buf, "hipEventRecord: HIP error %d (%s)", (int)e, hipGetErrorString(e));
+    return fail(ZERO_EHIP, buf);
+  }
+  return ZERO_OK;
+}
+
+}  // namespace zk

@@ -1,0 +1,115 @@
+// Internal declarations shared by the planner, the C ABI and the HIP launchers.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "zero_shard.h"
+
+struct zero_plan {
+  int32_t world = 0;
+  int64_t psi = 0;            // sum of tensor sizes
+  int64_t shard = 0;          // S = sum_b S_b
+  int64_t padded = 0;         // sum_b P_b
+  std::vector<int64_t> numel;
+  struct Bucket {
+    int32_t first, count;
+    int64_t numel, shard, padded, base, local_off;
+  };
+  std::vector<Bucket> buckets;
+  std::vector<int32_t> tensor_bucket;
+  std::vector<int64_t> tensor_offset;
+};
+
+namespace zk {
+
+// error state (thread-local message)
+int fail(int code, const std::string& msg);
+
+constexpr int kThreads = 256;   // threads per workgroup (4 wave64s)
+constexpr int kVec = 8;         // elements per thread per tile
+constexpr int kTile = kThreads * kVec;
+constexpr int kMaxSeg = 24;     // gather pieces one launch of the update kernel can address
+constexpr int kReduceBlocks = 2048;   // fixed grid of the gradient-preparation pass
+
+// A rank piece as seen by one launch: local elements [.., end) map to gather
+// element (local index + delta).
+struct Seg {
+  int64_t end;
+  int64_t delta;
+};
+
+struct AdamK {  // fp32 constants of one step
+  float b1, b2, omb1, omb2, bc1, bc2, lr, eps, dec;
+};
+
+struct StepLaunch {
+  // gradient source
+  const void* grad;
+  int64_t ld_bytes;       // slice stride in bytes
+  int32_t n;              // N
+  int32_t n_pow2;         // N is a power of two: acc * (1/N) is the IEEE quotient
+  float nf;               // float(N)
+  float recip_n;          // 1/N (exact when n_pow2)
+  float inv_scale;
+  const float* g_stash;   // stash mode when non-null
+  const float* clip;      // stash mode multiplier (may be null)
+  // state
+  const float* p_in;
+  const float* m_in;
+  const float* v_in;
+  float* p_out;
+  float* m_out;
+  float* v_out;
+  char* gather;
+  AdamK c;
+  const uint32_t* skip_in;
+  uint32_t* overflow;
+  // local vector range of this launch and its pieces
+  int64_t S;              // shard length (elements at or past S do not exist)
+  int64_t v_lo, v_hi;     // vectors [v_lo, v_hi) of kVec elements
+  int32_t nseg;
+  Seg seg[kMaxSeg];
+};
+
+struct ReduceLaunch {
+  const void* grad;
+  int64_t ld_bytes;
+  int32_t n;
+  int32_t n_pow2;
+  float nf, recip_n, inv_scale;
+  float* g_out;
+  uint32_t* ws_flags;     // [gridDim.x]
+  double* ws_sums;        // [gridDim.x]
+  int32_t want_sumsq;
+  int64_t S;
+  int64_t nvec;           // ceil(S / kVec)
+};
+
+struct NormLaunch {
+  const uint32_t* ws_flags;
+  const double* ws_sums;
+  int32_t nblocks;
+  double other_sumsq;
+  double max_norm;
+  uint32_t* overflow_out;
+  double* sumsq_out;
+  float* clip_out;
+};
+
+// workspace layout
+inline size_t ws_flags_offset() { return 0; }
+inline size_t ws_sums_offset() { return (size_t)kReduceBlocks * sizeof(uint32_t); }
+inline size_t ws_bytes() { return ws_sums_offset() + (size_t)kReduceBlocks * sizeof(double); }
+
+// launchers (kernels.hip); return ZERO_OK or ZERO_EHIP
+int launch_fill_u32(uint32_t* p, uint32_t value, void* stream);
+int launch_step(const StepLaunch& a, zero_dtype_t gt, zero_dtype_t pt, bool stash, void* stream);
+int launch_recast(const StepLaunch& a, zero_dtype_t pt, const uint32_t* cond, void* stream);
+int launch_reduce(const ReduceLaunch& a, zero_dtype_t gt, int32_t nblocks, void* stream);
+int launch_norm(const NormLaunch& a, void* stream);
+int record_event(void* ev, void* stream);
+
+}  // namespace zk

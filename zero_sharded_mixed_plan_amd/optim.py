@@ -1,0 +1,156 @@
+"""ZeroAdam: one rank's sharded mixed-precision AdamW over torch device tensors.
+
+The object mirrors the surface of the handbook's ZeroAdam ("ZeRO 与 FSDP：
+切分优化器状态、梯度与参数", section "从零实现 ZeRO 的 Adam": constructor with
+lr, betas, eps; step(); state_bytes()) for one rank on one GPU, with the mixed
+precision parts of "PaddlePaddle ZeRO优化…" (section "混合精度才是最佳拍档":
+scale, unscale, skip on overflow, update the scale).  torch supplies device
+memory and the stream; every step of the computation runs in libzero_shard.so.
+
+The reduce-scatter's input arrives as `slices`, an [N, ld] device tensor whose row
+k holds rank k's gradient of this rank's shard (in a multi-GPU job these rows
+are what the reduce-scatter would sum).  The new parameters land in this rank's
+slots of `gather`, the all-gather buffer.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from . import _abi
+
+_CODES = {torch.float32: _abi.ZERO_F32, torch.bfloat16: _abi.ZERO_BF16, torch.float16: _abi.ZERO_F16}
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    try:
+        return _CODES[dt]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {dt}") from None
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+class ZeroAdam:
+    """Sharded AdamW state and step of rank `rank` out of `world`.
+
+    Without clipping the step is one fused pass over the N slices and writes the
+    new state into the second of two state buffers, which become current only
+    if no gradient overflowed.  With max_norm > 0 the step is two passes: the
+    reduced gradient and the norm partials first, then the update in place.
+    Loss-scale policy (the pages show only GradScaler's API): the scale halves on
+    an overflow and doubles after `growth_interval` clean steps.
+    """
+
+    def __init__(self, numels: Sequence[int], world: int, rank: int, *, lr: float,
+                 betas=(0.9, 0.999), eps: float = 1e-8, weight_decay: float = 0.0,
+                 bucket_cap: int = 0, grad_dtype=torch.bfloat16, param_dtype=torch.bfloat16,
+                 max_norm: float = 0.0, loss_scale: float = 1.0, dynamic_loss_scale: bool = False,
+                 growth_interval: int = 2000, master: Optional[torch.Tensor] = None,
+                 gather: Optional[torch.Tensor] = None, device="cuda"):
+        self.plan = _abi.Plan(numels, world, bucket_cap)
+        self.world, self.rank = int(world), int(rank)
+        self.lr, self.betas, self.eps, self.weight_decay = lr, tuple(betas), eps, weight_decay
+        self.grad_dtype, self.param_dtype = grad_dtype, param_dtype
+        self.max_norm = float(max_norm)
+        self.loss_scale = float(loss_scale)
+        self.dynamic = dynamic_loss_scale
+        self.growth_interval = growth_interval
+        self._clean = 0
+        self.t = 0
+        self.skipped = 0
+        S = self.plan.shard_numel
+        self.S = S
+        dev = torch.device(device)
+        f32 = dict(dtype=torch.float32, device=dev)
+        n_sets = 1 if self.max_norm > 0 else 2
+        self._state = [[torch.zeros(S, **f32) for _ in range(3)] for _ in range(n_sets)]
+        self._cur = 0
+        if master is not None:
+            self._state[0][0].copy_(master)
+        self.gather = gather if gather is not None else torch.zeros(
+            self.plan.padded_numel, dtype=param_dtype, device=dev)
+        if self.gather.numel() != self.plan.padded_numel or self.gather.dtype != param_dtype:
+            raise ValueError("gather buffer has the wrong size or dtype")
+        self.flag = torch.zeros(1, dtype=torch.int32, device=dev)
+        if self.max_norm > 0:
+            self.g = torch.empty(S, **f32)
+            self.ws = torch.empty(self.plan.workspace_bytes(), dtype=torch.uint8, device=dev)
+            self.sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+            self.clip = torch.ones(1, **f32)
+
+    # -- state ---------------------------------------------------------------
+    @property
+    def master(self) -> torch.Tensor:
+        return self._state[self._cur][0]
+
+    @property
+    def m(self) -> torch.Tensor:
+        return self._state[self._cur][1]
+
+    @property
+    def v(self) -> torch.Tensor:
+        return self._state[self._cur][2]
+
+    def state_bytes(self) -> int:
+        """fp32 master + m + v of this rank (the handbook's state_bytes())."""
+        return 3 * 4 * self.S
+
+    def segments(self):
+        return self.plan.segments(self.rank)
+
+    # -- step ----------------------------------------------------------------
+    def step(self, slices: torch.Tensor, other_ranks_sumsq: float = 0.0) -> bool:
+        """One step from an [N, ld] slice tensor; returns False if it was skipped."""
+        if slices.dim() != 2 or slices.shape[0] != self.world or slices.shape[1] < self.S:
+            raise ValueError("slices must be [N, ld >= S]")
+        if slices.dtype != self.grad_dtype or slices.stride(1) != 1:
+            raise ValueError("slices have the wrong dtype or layout")
+        st = _stream()
+        gcode = dtype_code(slices.dtype)
+        inv = 1.0 / self.loss_scale
+        b1, b2 = self.betas
+        common = dict(rank=self.rank, gather=self.gather.data_ptr(),
+                      param_dtype=dtype_code(self.param_dtype), lr=self.lr, beta1=b1, beta2=b2,
+                      eps=self.eps, weight_decay=self.weight_decay, step=self.t + 1)
+        if self.max_norm > 0:
+            _abi.zero_reduce_shard(self.plan, slices.data_ptr(), slices.stride(0), gcode, inv,
+                                   self.g.data_ptr(), self.ws.data_ptr(), True, st)
+            _abi.zero_shard_norm(self.plan, self.ws.data_ptr(), other_ranks_sumsq, self.max_norm,
+                                 self.flag.data_ptr(), self.sumsq.data_ptr(), self.clip.data_ptr(), st)
+            p, m, v = self._state[0]
+            args = _abi.adam_args(g_stash=self.g.data_ptr(), clip_coef=self.clip.data_ptr(),
+                                  master_in=p.data_ptr(), m_in=m.data_ptr(), v_in=v.data_ptr(),
+                                  master_out=p.data_ptr(), m_out=m.data_ptr(), v_out=v.data_ptr(),
+                                  skip_in=self.flag.data_ptr(), **common)
+            _abi.zero_adam_step(self.plan, args, st)
+            ok = int(self.flag.item()) == 0
+        else:
+            src, dst = self._state[self._cur], self._state[1 - self._cur]
+            args = _abi.adam_args(grad=slices.data_ptr(), grad_ld=slices.stride(0), grad_dtype=gcode,
+                                  inv_scale=inv, master_in=src[0].data_ptr(), m_in=src[1].data_ptr(),
+                                  v_in=src[2].data_ptr(), master_out=dst[0].data_ptr(),
+                                  m_out=dst[1].data_ptr(), v_out=dst[2].data_ptr(),
+                                  overflow_out=self.flag.data_ptr(), **common)
+            _abi.zero_adam_step(self.plan, args, st)
+            ok = int(self.flag.item()) == 0
+            if ok:
+                self._cur = 1 - self._cur
+        self._update_scale(ok)
+        return ok
+
+    def _update_scale(self, ok: bool) -> None:
+        if ok:
+            self.t += 1
+            self._clean += 1
+            if self.dynamic and self._clean >= self.growth_interval:
+                self.loss_scale *= 2.0
+                self._clean = 0
+        else:
+            self.skipped += 1
+            self._clean = 0
+            if self.dynamic:
+                self.loss_scale *= 0.5
