@@ -159,7 +159,7 @@ int zero_reduce_shard(const zero_plan_t* plan, const void* grad, int64_t grad_ld
  * Errors: ZERO_EINVAL, ZERO_EHIP.
  */
 int zero_shard_norm(const zero_plan_t* plan, const void* ws, double other_ranks_sumsq,
-                    float max_norm, uint32_t* overflow_out, double* sumsq_out,
+                    double max_norm, uint32_t* overflow_out, double* sumsq_out,
                     float* clip_coef_out, void* stream);
 
 /* Arguments of zero_adam_step (host struct; pointers are device addresses). */

@@ -95,7 +95,7 @@ def lib() -> ctypes.CDLL:
         "zero_plan_bytes": (ctypes.c_int, [vp, i32, ctypes.POINTER(f64), P64]),
         "zero_workspace_bytes": (ctypes.c_size_t, [vp]),
         "zero_reduce_shard": (ctypes.c_int, [vp, vp, i64, ctypes.c_int, f32, vp, vp, i32, vp]),
-        "zero_shard_norm": (ctypes.c_int, [vp, vp, f64, f32, vp, vp, vp, vp]),
+        "zero_shard_norm": (ctypes.c_int, [vp, vp, f64, f64, vp, vp, vp, vp]),
         "zero_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(zero_adam_args_t), vp]),
         "zero_last_error": (ctypes.c_char_p, []),
         "zero_version": (ctypes.c_char_p, []),

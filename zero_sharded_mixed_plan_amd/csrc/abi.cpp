@@ -108,7 +108,7 @@ extern "C" int zero_reduce_shard(const zero_plan_t* plan, const void* grad, int6
 }
 
 extern "C" int zero_shard_norm(const zero_plan_t* plan, const void* ws, double other_ranks_sumsq,
-                               float max_norm, uint32_t* overflow_out, double* sumsq_out,
+                               double max_norm, uint32_t* overflow_out, double* sumsq_out,
                                float* clip_coef_out, void* stream) {
   if (!plan) return fail(ZERO_EINVAL, "zero_shard_norm: plan is NULL");
   if (!ws) return fail(ZERO_EINVAL, "zero_shard_norm: workspace is NULL");
@@ -124,7 +124,7 @@ extern "C" int zero_shard_norm(const zero_plan_t* plan, const void* ws, double o
   a.ws_sums = reinterpret_cast<const double*>(static_cast<const char*>(ws) + zk::ws_sums_offset());
   a.nblocks = reduce_grid(plan->shard);
   a.other_sumsq = other_ranks_sumsq;
-  a.max_norm = (double)max_norm;
+  a.max_norm = max_norm;
   a.overflow_out = overflow_out;
   a.sumsq_out = sumsq_out;
   a.clip_out = clip_coef_out;
