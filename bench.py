@@ -266,6 +266,29 @@ def run(name, steps, warmup, with_cpu):
     return out
 
 
+def copy_probe(steps, warmup, gib=4.0):
+    """A plain device-to-device copy kernel of known size (torch's elementwise
+    multiply by 1 over fp32): reference bandwidth on this GPU, and the counter
+    calibration (HBM bytes read and written per launch are both 4 * n)."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        torch.mul(src, 1.0, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    out = {"probe": "copy", "elements": n, "bytes_read": 4 * n, "bytes_written": 4 * n,
+           "ms_per_launch": ms, "GBps": 8 * n / (ms * 1e-3) / 1e9}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,11 +297,15 @@ def main():
     ap.add_argument("--workload", default=DEFAULT)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline")
     ap.add_argument("--report", default=None, help="append every workload's JSON line here")
+    ap.add_argument("--copy-probe", action="store_true", help="time a plain copy kernel only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one rank on one GPU; --gpus {args.gpus} is not "
               "supported (the multi-GPU collectives are out of scope)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.steps, args.warmup)
+        return
     import workloads as W
     names = W.ORDER if args.workload == "all" else [args.workload]
     if args.workload != "all" and args.workload not in W.FULL:

@@ -1,0 +1,155 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the
+benchmark times (slice stride rounded up to 64 elements, one-shot grids).
+
+The step is elementwise, so the oracle computes sampled elements one by one:
+2^18 random local indices plus every piece boundary and the shard's ends.
+Properties that hold at any size cover the rest: the gather buffer outside the
+rank's pieces is untouched, the overflow flag is exact, and the norm equals a
+float64 library sum over the GPU's reduced gradient (whose sampled elements are
+bit-exact against the oracle)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+import zero_sharded_mixed_plan_amd as Z
+from gpu_harness import CODE, check_params, compare_step, oracle_layout, say, storage
+from oracle import casts as OC
+from oracle import step as OS
+
+pytestmark = pytest.mark.gpu
+F = np.float32
+SENTINEL = {"f32": 7.0, "bf16": -3.0, "f16": 5.0}
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.empty_cache()
+
+
+def _sample_idx(S, segments, n=1 << 18, seed=0):
+    rng = np.random.default_rng(seed)
+    idx = [rng.integers(0, S, n)]
+    edges = [0, S]
+    for _goff, lo, ln, valid in segments:
+        edges += [lo, lo + ln, lo + valid]
+    for e in edges:
+        idx.append(np.arange(max(0, e - 16), min(S, e + 16)))
+    return np.unique(np.concatenate(idx)).astype(np.int64)
+
+
+def _take(t, idx_dev):
+    return storage(t.index_select(0, idx_dev))
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_full_size(name):
+    w = W.FULL[name]
+    pl, lay = oracle_layout(w)
+    S = lay.S
+    dev = torch.device("cuda")
+    plan = Z.Plan(W.numels(w.tensors), w.world, w.bucket_cap)
+    assert plan.shard_numel == S and plan.segments(w.rank) == lay.segments
+    ld = (S + 63) // 64 * 64
+    say(f"full {name}: S={S} N={w.world} rank={w.rank} pieces={len(lay.segments)} ld={ld}")
+    A = list(W.make_state(w, lay, dev))
+    B = [torch.empty_like(x) for x in A]
+    pdt = W.torch_dtype(w.param_dtype)
+    gather = torch.full((pl.padded_numel,), SENTINEL[w.param_dtype], dtype=pdt, device=dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    clip = w.max_norm > 0
+    if clip:
+        g = torch.empty(S, dtype=torch.float32, device=dev)
+        ws = torch.empty(plan.workspace_bytes(), dtype=torch.uint8, device=dev)
+        sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+        coef = torch.zeros(1, dtype=torch.float32, device=dev)
+    idx = _sample_idx(S, lay.segments, seed=w.seed)
+    idx_dev = torch.from_numpy(idx).to(dev)
+    # local index -> gather index for the sampled elements
+    gidx = np.empty_like(idx)
+    for goff, lo, ln, _v in lay.segments:
+        sel = (idx >= lo) & (idx < lo + ln)
+        gidx[sel] = idx[sel] - lo + goff
+    gidx_dev = torch.from_numpy(gidx).to(dev)
+    st = torch.cuda.current_stream().cuda_stream
+    cur, nxt = A, B
+    t = w.t0
+    slices = None
+    steps = 3 if w.inject_inf_step is not None else 1
+    for step in range(1, steps + 1):
+        slices = W.make_slices(w, lay, step=step, ld=ld, device=dev, out=slices)
+        p_in, m_in, v_in = (_take(x, idx_dev) for x in cur)
+        sl = [_take(slices[k, :S], idx_dev) for k in range(w.world)]
+        common = dict(rank=w.rank, gather=gather.data_ptr(), param_dtype=CODE[w.param_dtype],
+                      lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                      weight_decay=w.weight_decay, step=t + 1)
+        kw = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                  t=t + 1, inv_scale=1.0 / w.loss_scale)
+        if clip:
+            Z.zero_reduce_shard(plan, slices.data_ptr(), ld, CODE[w.grad_dtype], 1.0 / w.loss_scale,
+                                g.data_ptr(), ws.data_ptr(), True, st)
+            Z.zero_shard_norm(plan, ws.data_ptr(), 0.0, w.max_norm, flag.data_ptr(),
+                              sumsq.data_ptr(), coef.data_ptr(), st)
+            p, m, v = cur
+            a = Z.adam_args(g_stash=g.data_ptr(), clip_coef=coef.data_ptr(), master_in=p.data_ptr(),
+                            m_in=m.data_ptr(), v_in=v.data_ptr(), master_out=p.data_ptr(),
+                            m_out=m.data_ptr(), v_out=v.data_ptr(), skip_in=flag.data_ptr(), **common)
+            Z.zero_adam_step(plan, a, st)
+            torch.cuda.synchronize()
+            q = float(sumsq.item())
+            q_lib = float(torch.sum(g.double() * g.double()).item())
+            assert abs(q - q_lib) <= 1e-9 * q_lib, (q, q_lib)
+            c32 = F(coef.item())
+            assert c32 == OS.clip_coefficient(q, w.max_norm)
+            res = OS.shard_step(sl, w.grad_dtype, w.param_dtype, w.world, p_in, m_in, v_in,
+                                max_norm=w.max_norm, clip_override=c32, **kw)
+            assert np.array_equal(_take(g, idx_dev).view(np.uint32), res.g.view(np.uint32))
+            out = cur
+            say(f"  q={q:.6g} norm={np.sqrt(q):.6g} clip={float(c32):.6g}")
+        else:
+            a = Z.adam_args(grad=slices.data_ptr(), grad_ld=ld, grad_dtype=CODE[w.grad_dtype],
+                            inv_scale=1.0 / w.loss_scale, master_in=cur[0].data_ptr(),
+                            m_in=cur[1].data_ptr(), v_in=cur[2].data_ptr(),
+                            master_out=nxt[0].data_ptr(), m_out=nxt[1].data_ptr(),
+                            v_out=nxt[2].data_ptr(), overflow_out=flag.data_ptr(), **common)
+            Z.zero_adam_step(plan, a, st)
+            torch.cuda.synchronize()
+            res = OS.shard_step(sl, w.grad_dtype, w.param_dtype, w.world, p_in, m_in, v_in, **kw)
+        flag_gpu = int(flag.item())
+        injected = w.inject_inf_step == step
+        say(f"  step {step}: flag {flag_gpu} (injected inf: {injected})")
+        assert flag_gpu == int(injected)
+        if not clip:
+            # a sample may miss the injected element: the flag is decided on the whole shard
+            out = cur if flag_gpu else nxt
+        gp, gm, gv = (_take(x, idx_dev) for x in out)
+        if injected:
+            for a_, b_ in ((gp, p_in), (gm, m_in), (gv, v_in)):
+                assert np.array_equal(a_.view(np.uint32), b_.view(np.uint32))
+        else:
+            g_used = res.g if not clip else np.multiply(res.g, res.clip, dtype=F)
+            n, tot = compare_step(gp, gm, gv, res, p_in, m_in, v_in, g_used,
+                                  OS.adam_consts(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay,
+                                                 t + 1), f"{name} step {step}")
+            assert n == tot, f"{tot - n} sampled state elements differ in the last bit"
+        # the sampled gather elements hold the rounded master the state now has
+        want = OC.narrow(gp, w.param_dtype)
+        got = _take(gather, gidx_dev)
+        check_params(got, want, w.param_dtype, f"{name} step {step} params")
+        if not flag_gpu:
+            t += 1
+            if not clip:
+                cur, nxt = nxt, cur
+    # nothing outside the rank's pieces was written
+    sent = torch.tensor(SENTINEL[w.param_dtype], dtype=pdt, device=dev)
+    prev = 0
+    for goff, _lo, ln, _v in sorted(lay.segments):
+        if goff > prev:
+            assert bool(torch.all(gather[prev:goff] == sent)), f"write before piece at {goff}"
+        prev = goff + ln
+    if prev < pl.padded_numel:
+        assert bool(torch.all(gather[prev:] == sent)), "write after the last piece"
+    del A, B, gather, slices

@@ -33,6 +33,29 @@ struct TF32 { static constexpr int bytes = 4; };
 struct TBF16 { static constexpr int bytes = 2; };
 struct TF16 { static constexpr int bytes = 2; };
 
+// Cache hints.  Gradient slices are read exactly once per step and the gather
+// slot is written once and only read by the all-gather, so both move with the
+// non-temporal bit (measured on the GPT-2 1.5B shard: +4% over plain loads and
+// stores; non-temporal hints on the fp32 state made it slower).
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ void st_stream16(void* p, uint4 x) {
+  const v4u y = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(y, reinterpret_cast<v4u*>(p));
+}
+__device__ __forceinline__ void st_stream8(void* p, uint2 x) {
+  const v2u y = {x.x, x.y};
+  __builtin_nontemporal_store(y, reinterpret_cast<v2u*>(p));
+}
+__device__ __forceinline__ void st_stream4(void* p, uint32_t x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<uint32_t*>(p));
+}
+
 // 8 elements of a slice, raw: one uint4 for 16-bit types, two for fp32.
 template <class T>
 struct Raw { uint4 q[T::bytes / 2]; };
@@ -41,7 +64,7 @@ template <class T>
 __device__ __forceinline__ Raw<T> ld_raw(const char* p) {
   Raw<T> r;
 #pragma unroll
-  for (int i = 0; i < T::bytes / 2; ++i) r.q[i] = reinterpret_cast<const uint4*>(p)[i];
+  for (int i = 0; i < T::bytes / 2; ++i) r.q[i] = ld_stream16(p + 16 * i);
   return r;
 }
 
@@ -105,14 +128,13 @@ __device__ __forceinline__ void store_words(char* dst, const u32* w) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(dst);
   if ((a & 15) == 0) {
 #pragma unroll
-    for (int i = 0; i < NW; i += 4)
-      *reinterpret_cast<uint4*>(dst + 4 * i) = make_uint4(w[i], w[i + 1], w[i + 2], w[i + 3]);
+    for (int i = 0; i < NW; i += 4) st_stream16(dst + 4 * i, make_uint4(w[i], w[i + 1], w[i + 2], w[i + 3]));
   } else if ((a & 7) == 0) {
 #pragma unroll
-    for (int i = 0; i < NW; i += 2) *reinterpret_cast<uint2*>(dst + 4 * i) = make_uint2(w[i], w[i + 1]);
+    for (int i = 0; i < NW; i += 2) st_stream8(dst + 4 * i, make_uint2(w[i], w[i + 1]));
   } else if ((a & 3) == 0) {
 #pragma unroll
-    for (int i = 0; i < NW; ++i) *reinterpret_cast<u32*>(dst + 4 * i) = w[i];
+    for (int i = 0; i < NW; ++i) st_stream4(dst + 4 * i, w[i]);
   } else {  // 2-byte aligned 16-bit elements
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
