@@ -298,6 +298,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline")
     ap.add_argument("--report", default=None, help="append every workload's JSON line here")
     ap.add_argument("--copy-probe", action="store_true", help="time a plain copy kernel only")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="first run a plain copy of known size (torch.neg over 2^28 fp32, 3 "
+                         "launches) in this process, to scale HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one rank on one GPU; --gpus {args.gpus} is not "
@@ -306,6 +309,15 @@ def main():
     if args.copy_probe:
         copy_probe(args.steps, args.warmup)
         return
+    if args.copy_calibrate:
+        import torch
+        src = torch.randn(1 << 28, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x torch.neg over 2^28 fp32 (1 GiB read + 1 GiB written)")
+        del src, dst
     import workloads as W
     names = W.ORDER if args.workload == "all" else [args.workload]
     if args.workload != "all" and args.workload not in W.FULL:
