@@ -122,9 +122,10 @@ int zero_plan_bytes(const zero_plan_t* plan, int32_t stage, double* formula_byte
 /* ------------------------------------------------------------------------ */
 
 /*
- * Bytes of device workspace that zero_reduce_shard / zero_shard_norm need
- * (per-workgroup overflow words and float64 partial sums).  Caller-allocated,
- * 16-byte aligned, no initial content required.  0 for a NULL plan.
+ * Bytes of device workspace that zero_reduce_shard / zero_shard_norm need: one
+ * float64 partial sum and one overflow word per 2048 shard elements (about
+ * 6 bytes per 1000 elements).  Caller-allocated, 16-byte aligned, no initial
+ * content required.  0 for a NULL plan.
  */
 size_t zero_workspace_bytes(const zero_plan_t* plan);
 

@@ -10,7 +10,9 @@ import ctypes
 import os
 from typing import List, Tuple
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzero_shard.so")
+# ZERO_SHARD_LIB selects another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("ZERO_SHARD_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libzero_shard.so")
 
 ZERO_OK, ZERO_EINVAL, ZERO_EALIGN, ZERO_ENOMEM, ZERO_EHIP = 0, -1, -2, -3, -4
 ZERO_F32, ZERO_BF16, ZERO_F16 = 0, 1, 2
@@ -69,15 +71,20 @@ _lib = None
 def lib() -> ctypes.CDLL:
     """Load the library once.  Fails loudly when it has not been built."""
     global _lib
-    if _lib is not None:
-        return _lib
+    if _lib is None:
+        _lib = load(LIB_PATH)
+    return _lib
+
+
+def load(path: str) -> ctypes.CDLL:
+    """Load one build of the library from `path` and declare its C signatures."""
     # torch first: the library must bind to the HIP runtime torch already uses
     # for the device memory and streams it hands over (one runtime per process)
     import torch  # noqa: F401
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with "
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
                           "`python -m zero_sharded_mixed_plan_amd.build` (hipcc, gfx950)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     i32, i64, vp, f32, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_double
     P64, P32 = ctypes.POINTER(i64), ctypes.POINTER(i32)
     sig = {
@@ -104,7 +111,6 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = L
     return L
 
 

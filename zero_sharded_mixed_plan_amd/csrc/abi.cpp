@@ -67,12 +67,6 @@ void slice_consts(int32_t n, int32_t* n_pow2, float* nf, float* recip) {
   *recip = (float)(1.0 / (double)n);
 }
 
-int reduce_grid(int64_t S) {
-  const int64_t nvec = (S + zk::kVec - 1) / zk::kVec;
-  const int64_t b = (nvec + zk::kThreads - 1) / zk::kThreads;
-  return (int)(b < zk::kReduceBlocks ? b : zk::kReduceBlocks);
-}
-
 }  // namespace
 
 extern "C" int zero_reduce_shard(const zero_plan_t* plan, const void* grad, int64_t grad_ld,
@@ -99,12 +93,12 @@ extern "C" int zero_reduce_shard(const zero_plan_t* plan, const void* grad, int6
   slice_consts(a.n, &a.n_pow2, &a.nf, &a.recip_n);
   a.inv_scale = inv_scale;
   a.g_out = g_out;
-  a.ws_flags = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + zk::ws_flags_offset());
+  a.ws_flags = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + zk::ws_flags_offset(S));
   a.ws_sums = reinterpret_cast<double*>(static_cast<char*>(ws) + zk::ws_sums_offset());
   a.want_sumsq = want_sumsq ? 1 : 0;
   a.S = S;
   a.nvec = (S + zk::kVec - 1) / zk::kVec;
-  return zk::launch_reduce(a, grad_dtype, reduce_grid(S), stream);
+  return zk::launch_reduce(a, grad_dtype, zk::reduce_blocks(S), stream);
 }
 
 extern "C" int zero_shard_norm(const zero_plan_t* plan, const void* ws, double other_ranks_sumsq,
@@ -120,9 +114,9 @@ extern "C" int zero_shard_norm(const zero_plan_t* plan, const void* ws, double o
       (overflow_out && !aligned(overflow_out, 4)))
     return fail(ZERO_EALIGN, "zero_shard_norm: misaligned output");
   zk::NormLaunch a{};
-  a.ws_flags = reinterpret_cast<const uint32_t*>(static_cast<const char*>(ws) + zk::ws_flags_offset());
+  a.ws_flags = reinterpret_cast<const uint32_t*>(static_cast<const char*>(ws) + zk::ws_flags_offset(plan->shard));
   a.ws_sums = reinterpret_cast<const double*>(static_cast<const char*>(ws) + zk::ws_sums_offset());
-  a.nblocks = reduce_grid(plan->shard);
+  a.nblocks = zk::reduce_blocks(plan->shard);
   a.other_sumsq = other_ranks_sumsq;
   a.max_norm = max_norm;
   a.overflow_out = overflow_out;

@@ -206,41 +206,42 @@ __device__ __forceinline__ void adamw1(float& p, float& m, float& v, float g, co
 }
 
 // Sum of N slices for 8 elements: acc = s_0, then acc += s_k in ascending k.
-// Loads go out in batches of NB before their adds so a wave keeps NB * 1 KiB in
-// flight per batch.
+// Software-pipelined: every load of a batch of NB slices is issued before the
+// first add, and the next batch's loads go out before this batch's adds, so a
+// wave keeps up to 2 * NB KiB in flight and never waits on one slice alone.
 template <class T, int NB>
 __device__ __forceinline__ void reduce8(const char* base, int64_t ld_bytes, int n, float acc[8]) {
-  const Raw<T> r0 = ld_raw<T>(base);
-  int k = 1;
-  for (; k + NB <= n; k += NB) {
-    Raw<T> r[NB];
+  Raw<T> cur[NB], nxt[NB];
+  int cnt = n < NB ? n : NB;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) r[b] = ld_raw<T>(base + (int64_t)(k + b) * ld_bytes);
-    if (k == 1) widen8<T>(r0, acc);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float w[8];
-      widen8<T>(r[b], w);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + w[e];
-    }
-  }
-  if (k == 1) widen8<T>(r0, acc);
-  const int rest = n - k;  // < NB, uniform
-  if (rest > 0) {
-    Raw<T> r[NB];
+  for (int b = 0; b < NB; ++b)
+    if (b < cnt) cur[b] = ld_raw<T>(base + (int64_t)b * ld_bytes);
+  int k0 = 0;
+  while (true) {
+    const int k1 = k0 + cnt;
+    const int rem = n - k1;
+    const int cnt1 = rem < NB ? rem : NB;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
-      if (b < rest) r[b] = ld_raw<T>(base + (int64_t)(k + b) * ld_bytes);
+      if (b < cnt1) nxt[b] = ld_raw<T>(base + (int64_t)(k1 + b) * ld_bytes);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      if (b < rest) {
+      if (b < cnt) {
         float w[8];
-        widen8<T>(r[b], w);
+        widen8<T>(cur[b], w);
+        if (k0 == 0 && b == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + w[e];
+          for (int e = 0; e < 8; ++e) acc[e] = w[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = acc[e] + w[e];
+        }
       }
     }
+    if (cnt1 <= 0) break;
+    for (int b = 0; b < NB; ++b) cur[b] = nxt[b];
+    k0 = k1;
+    cnt = cnt1;
   }
 }
 
@@ -251,8 +252,10 @@ __device__ __forceinline__ float reduce1(const char* base, int64_t ld_bytes, int
   return acc;
 }
 
-template <class T> struct Batch { static constexpr int value = 8; };
-template <> struct Batch<TF32> { static constexpr int value = 4; };
+// Slices per load batch: 8 (one batch holds all of N <= 8), 16 for larger N;
+// fp32 slices are twice as wide, so half as many.
+template <class T, bool WIDE> struct Batch { static constexpr int value = WIDE ? 16 : 8; };
+template <bool WIDE> struct Batch<TF32, WIDE> { static constexpr int value = WIDE ? 8 : 4; };
 
 // gather index offset of local element j (uniform loop over the launch's pieces)
 __device__ __forceinline__ int64_t delta_of(const StepLaunch& a, int64_t j) {
@@ -266,7 +269,7 @@ __device__ __forceinline__ int64_t delta_of(const StepLaunch& a, int64_t j) {
 // the update kernel (fused: N slices in; stash: fp32 g in)
 // ---------------------------------------------------------------------------
 
-template <class GT, class PT, bool STASH>
+template <class GT, class PT, bool STASH, bool WIDE>
 __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
   if (a.skip_in != nullptr && *a.skip_in != 0u) {
     // skipped by the caller: report it like an overflow so the fused step's
@@ -292,8 +295,8 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
       for (int e = 0; e < 8; ++e) g[e] = g[e] * clip;
     } else {
       float acc[8];
-      reduce8<GT, Batch<GT>::value>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes,
-                                    a.n, acc);
+      reduce8<GT, Batch<GT, WIDE>::value>(static_cast<const char*>(a.grad) + j0 * GT::bytes,
+                                          a.ld_bytes, a.n, acc);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, a.inv_scale);
@@ -368,16 +371,19 @@ __device__ __forceinline__ double wave_sum(double x) {
   return x;
 }
 
-template <class GT>
+template <class GT, bool WIDE>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) {
+  // one 8-element vector per thread; workgroup b owns vectors [256 b, 256 b + 256),
+  // so the partition (and every partial sum) depends only on S
   double sq = 0.0;
   bool bad = false;
-  for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < a.nvec;
-       v += (int64_t)gridDim.x * kThreads) {
+  const int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (v < a.nvec) {
     const int64_t j0 = v * kVec;
     if (j0 + kVec <= a.S) {
       float acc[8], g[8];
-      reduce8<GT, Batch<GT>::value>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes, a.n, acc);
+      reduce8<GT, Batch<GT, WIDE>::value>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes,
+                                          a.n, acc);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, a.inv_scale);
@@ -424,19 +430,19 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) 
 
 // One workgroup: OR of the overflow words, fixed-order sum of the partials,
 // global norm and clip coefficient.
-__global__ __launch_bounds__(kThreads) void norm_kernel(const NormLaunch a) {
+__global__ __launch_bounds__(kNormThreads) void norm_kernel(const NormLaunch a) {
   double s = 0.0;
   u32 f = 0;
-  for (int i = threadIdx.x; i < a.nblocks; i += kThreads) {
+  for (int64_t i = threadIdx.x; i < a.nblocks; i += kNormThreads) {
     s += a.ws_sums[i];
     f |= a.ws_flags[i];
   }
-  __shared__ double s_sum[kThreads];
-  __shared__ u32 s_f[kThreads];
+  __shared__ double s_sum[kNormThreads];
+  __shared__ u32 s_f[kNormThreads];
   s_sum[threadIdx.x] = s;
   s_f[threadIdx.x] = f;
   __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
+  for (int w = kNormThreads / 2; w > 0; w >>= 1) {
     if (threadIdx.x < w) {
       s_sum[threadIdx.x] += s_sum[threadIdx.x + w];
       s_f[threadIdx.x] |= s_f[threadIdx.x + w];
@@ -477,16 +483,40 @@ int launch_fill_u32(u32* p, u32 value, void* stream) {
 }
 
 template <class GT, class PT, bool STASH>
-static void go_step(const StepLaunch& a, unsigned blocks, hipStream_t st) {
-  hipLaunchKernelGGL((step_kernel<GT, PT, STASH>), dim3(blocks), dim3(kThreads), 0, st, a);
+static void go_step(const StepLaunch& a, unsigned blocks, size_t lds, hipStream_t st) {
+  if (!STASH && a.n > 8)
+    hipLaunchKernelGGL((step_kernel<GT, PT, STASH, true>), dim3(blocks), dim3(kThreads), lds, st, a);
+  else
+    hipLaunchKernelGGL((step_kernel<GT, PT, STASH, false>), dim3(blocks), dim3(kThreads), lds, st, a);
+}
+
+// Resident workgroups per CU of the streaming kernels.  Fewer concurrent waves
+// keep fewer DRAM pages open per stream: on the GPT-2 1.5B and Llama-7B shards
+// 3 workgroups (12 wave64s) per CU stream 5% faster than the 4-5 the registers
+// allow, and 1 per CU is too few.  The cap is imposed by reserving LDS the
+// kernels do not otherwise use.
+static size_t occupancy_lds(int per_cu) {
+  static thread_local int dev_cached = -1;
+  static thread_local size_t lds_cu = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev != dev_cached) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess) v = 0;
+    lds_cu = (size_t)v;
+    dev_cached = dev;
+  }
+  if (lds_cu == 0) return 0;
+  return (lds_cu / (size_t)per_cu) / 512 * 512;
 }
 
 template <class GT, bool STASH>
 static int dispatch_pt(const StepLaunch& a, zero_dtype_t pt, unsigned blocks, hipStream_t st) {
+  const size_t lds = occupancy_lds(kStreamBlocksPerCU);
   switch (pt) {
-    case ZERO_F32: go_step<GT, TF32, STASH>(a, blocks, st); return ZERO_OK;
-    case ZERO_BF16: go_step<GT, TBF16, STASH>(a, blocks, st); return ZERO_OK;
-    case ZERO_F16: go_step<GT, TF16, STASH>(a, blocks, st); return ZERO_OK;
+    case ZERO_F32: go_step<GT, TF32, STASH>(a, blocks, lds, st); return ZERO_OK;
+    case ZERO_BF16: go_step<GT, TBF16, STASH>(a, blocks, lds, st); return ZERO_OK;
+    case ZERO_F16: go_step<GT, TF16, STASH>(a, blocks, lds, st); return ZERO_OK;
   }
   return fail(ZERO_EINVAL, "unsupported parameter dtype");
 }
@@ -526,19 +556,31 @@ int launch_recast(const StepLaunch& a, zero_dtype_t pt, const u32* cond, void* s
   return check_launch("recast");
 }
 
-int launch_reduce(const ReduceLaunch& a, zero_dtype_t gt, int32_t nblocks, void* stream) {
+int launch_reduce(const ReduceLaunch& a, zero_dtype_t gt, int64_t nblocks, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  const bool wide = a.n > 8;
+  const size_t lds = occupancy_lds(kStreamBlocksPerCU);
+  const dim3 grid((unsigned)nblocks), blk(kThreads);
   switch (gt) {
-    case ZERO_F32: hipLaunchKernelGGL(reduce_kernel<TF32>, dim3(nblocks), dim3(kThreads), 0, st, a); break;
-    case ZERO_BF16: hipLaunchKernelGGL(reduce_kernel<TBF16>, dim3(nblocks), dim3(kThreads), 0, st, a); break;
-    case ZERO_F16: hipLaunchKernelGGL(reduce_kernel<TF16>, dim3(nblocks), dim3(kThreads), 0, st, a); break;
+    case ZERO_F32:
+      if (wide) hipLaunchKernelGGL((reduce_kernel<TF32, true>), grid, blk, lds, st, a);
+      else hipLaunchKernelGGL((reduce_kernel<TF32, false>), grid, blk, lds, st, a);
+      break;
+    case ZERO_BF16:
+      if (wide) hipLaunchKernelGGL((reduce_kernel<TBF16, true>), grid, blk, lds, st, a);
+      else hipLaunchKernelGGL((reduce_kernel<TBF16, false>), grid, blk, lds, st, a);
+      break;
+    case ZERO_F16:
+      if (wide) hipLaunchKernelGGL((reduce_kernel<TF16, true>), grid, blk, lds, st, a);
+      else hipLaunchKernelGGL((reduce_kernel<TF16, false>), grid, blk, lds, st, a);
+      break;
     default: return fail(ZERO_EINVAL, "unsupported gradient dtype");
   }
   return check_launch("reduce");
 }
 
 int launch_norm(const NormLaunch& a, void* stream) {
-  hipLaunchKernelGGL(norm_kernel, dim3(1), dim3(kThreads), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(norm_kernel, dim3(1), dim3(kNormThreads), 0, (hipStream_t)stream, a);
   return check_launch("norm");
 }
 

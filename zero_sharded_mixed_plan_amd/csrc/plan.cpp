@@ -152,4 +152,4 @@ extern "C" int zero_plan_bytes(const zero_plan_t* p, int32_t stage, double* form
   return ZERO_OK;
 }
 
-extern "C" size_t zero_workspace_bytes(const zero_plan_t* p) { return p ? zk::ws_bytes() : 0; }
+extern "C" size_t zero_workspace_bytes(const zero_plan_t* p) { return p ? zk::ws_bytes(p->shard) : 0; }

@@ -32,7 +32,8 @@ constexpr int kThreads = 256;   // threads per workgroup (4 wave64s)
 constexpr int kVec = 8;         // elements per thread per tile
 constexpr int kTile = kThreads * kVec;
 constexpr int kMaxSeg = 24;     // gather pieces one launch of the update kernel can address
-constexpr int kReduceBlocks = 2048;   // fixed grid of the gradient-preparation pass
+constexpr int kNormThreads = 1024;    // the one-workgroup norm finalize
+constexpr int kStreamBlocksPerCU = 3; // resident workgroups per CU of the streaming kernels
 
 // A rank piece as seen by one launch: local elements [.., end) map to gather
 // element (local index + delta).
@@ -91,7 +92,7 @@ struct ReduceLaunch {
 struct NormLaunch {
   const uint32_t* ws_flags;
   const double* ws_sums;
-  int32_t nblocks;
+  int64_t nblocks;
   double other_sumsq;
   double max_norm;
   uint32_t* overflow_out;
@@ -99,16 +100,21 @@ struct NormLaunch {
   float* clip_out;
 };
 
-// workspace layout
-inline size_t ws_flags_offset() { return 0; }
-inline size_t ws_sums_offset() { return (size_t)kReduceBlocks * sizeof(uint32_t); }
-inline size_t ws_bytes() { return ws_sums_offset() + (size_t)kReduceBlocks * sizeof(double); }
+// gradient-preparation grid: one 8-element vector per thread, one workgroup per
+// kTile elements; the workspace holds one fp64 partial and one overflow word per
+// workgroup
+inline int64_t reduce_blocks(int64_t S) { return (S + kTile - 1) / kTile; }
+inline size_t ws_sums_offset() { return 0; }
+inline size_t ws_flags_offset(int64_t S) { return (size_t)reduce_blocks(S) * sizeof(double); }
+inline size_t ws_bytes(int64_t S) {
+  return (ws_flags_offset(S) + (size_t)reduce_blocks(S) * sizeof(uint32_t) + 255) / 256 * 256;
+}
 
 // launchers (kernels.hip); return ZERO_OK or ZERO_EHIP
 int launch_fill_u32(uint32_t* p, uint32_t value, void* stream);
 int launch_step(const StepLaunch& a, zero_dtype_t gt, zero_dtype_t pt, bool stash, void* stream);
 int launch_recast(const StepLaunch& a, zero_dtype_t pt, const uint32_t* cond, void* stream);
-int launch_reduce(const ReduceLaunch& a, zero_dtype_t gt, int32_t nblocks, void* stream);
+int launch_reduce(const ReduceLaunch& a, zero_dtype_t gt, int64_t nblocks, void* stream);
 int launch_norm(const NormLaunch& a, void* stream);
 int record_event(void* ev, void* stream);
 
