@@ -71,13 +71,15 @@ def load_traffic(kernel: str, workload: str):
 # the CPU oracle, timed on a bounded sample (cpu_baseline)
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(w, slices, state, S, target_s=12.0, max_elems=1 << 26, chunk=1 << 20):
+def cpu_baseline(w, slices, tiled_state, S, target_s=12.0, max_elems=1 << 26, chunk=1 << 20):
     import concurrent.futures as cf
 
     import numpy as np
     import torch
 
+    import zero_sharded_mixed_plan_amd as Z
     from oracle import step as OS
+    from zero_sharded_mixed_plan_amd.optim import unpack_state
 
     threads = max(1, min(os.cpu_count() or 1, 16))
     n = min(S, max_elems)
@@ -91,7 +93,8 @@ def cpu_baseline(w, slices, state, S, target_s=12.0, max_elems=1 << 26, chunk=1 
         return t.numpy()
 
     sl = [host(slices[k, :n]) for k in range(w.world)]
-    p, m, v = (host(x[:n]) for x in state)
+    T = Z.ZERO_STATE_TILE
+    p, m, v = (host(x) for x in unpack_state(tiled_state[:(n + T - 1) // T * 3 * T], n))
     kw = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
               t=w.t0 + 1, inv_scale=1.0 / w.loss_scale, max_norm=w.max_norm)
 
@@ -123,9 +126,10 @@ def run(name, steps, warmup, with_cpu):
 
     import workloads as W
     import zero_sharded_mixed_plan_amd as Z
-    from zero_sharded_mixed_plan_amd.optim import dtype_code
+    from zero_sharded_mixed_plan_amd.optim import dtype_code, pack_state, state_arg_dict
 
     w = W.FULL[name]
+    layout = Z.ZERO_STATE_TILED
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     plan = Z.Plan(W.numels(w.tensors), w.world, w.bucket_cap)
@@ -139,8 +143,10 @@ def run(name, steps, warmup, with_cpu):
     slices = W.make_slices(w, lay, step=1, ld=ld, device=dev)
     if w.inject_inf_step is not None:   # time clean steps: draw the slices of a clean step
         slices = W.make_slices(w, lay, step=w.inject_inf_step + 1, ld=ld, device=dev, out=slices)
-    A = list(W.make_state(w, lay, dev))
-    B = [torch.empty_like(x) for x in A]
+    p0, m0, v0 = W.make_state(w, lay, dev)
+    A = [pack_state(p0, m0, v0, plan.state_numel(layout))]
+    del p0, m0, v0
+    B = [torch.empty_like(A[0])]
     gather = torch.zeros(plan.padded_numel, dtype=W.torch_dtype(w.param_dtype), device=dev)
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     clip = w.max_norm > 0
@@ -179,23 +185,20 @@ def run(name, steps, warmup, with_cpu):
                 e_red1.record(stream)
             Z.zero_shard_norm(plan, ws.data_ptr(), 0.0, w.max_norm, flag.data_ptr(),
                               sumsq.data_ptr(), coef.data_ptr(), st)
-            p, m, v = state["cur"]
-            a = Z.adam_args(g_stash=g.data_ptr(), clip_coef=coef.data_ptr(), master_in=p.data_ptr(),
-                            m_in=m.data_ptr(), v_in=v.data_ptr(), master_out=p.data_ptr(),
-                            m_out=m.data_ptr(), v_out=v.data_ptr(), skip_in=flag.data_ptr(),
+            cur = state["cur"]
+            a = Z.adam_args(g_stash=g.data_ptr(), clip_coef=coef.data_ptr(), skip_in=flag.data_ptr(),
                             step=t, ev_begin=e_up0.cuda_event if e_up0 else None,
-                            ev_end=e_up1.cuda_event if e_up1 else None, **common)
+                            ev_end=e_up1.cuda_event if e_up1 else None,
+                            **state_arg_dict(layout, cur, cur), **common)
             Z.zero_adam_step(plan, a, st)
         else:
             e0, e1 = ev if ev else (None, None)
             src, dst = state["cur"], state["nxt"]
             a = Z.adam_args(grad=slices.data_ptr(), grad_ld=ld, grad_dtype=dtype_code(slices.dtype),
-                            inv_scale=1.0 / w.loss_scale, master_in=src[0].data_ptr(),
-                            m_in=src[1].data_ptr(), v_in=src[2].data_ptr(),
-                            master_out=dst[0].data_ptr(), m_out=dst[1].data_ptr(),
-                            v_out=dst[2].data_ptr(), overflow_out=flag.data_ptr(), step=t,
+                            inv_scale=1.0 / w.loss_scale, overflow_out=flag.data_ptr(), step=t,
                             ev_begin=e0.cuda_event if e0 else None,
-                            ev_end=e1.cuda_event if e1 else None, **common)
+                            ev_end=e1.cuda_event if e1 else None,
+                            **state_arg_dict(layout, src, dst), **common)
             Z.zero_adam_step(plan, a, st)
             # the data are finite, so every step commits: swap without a host read
             state["cur"], state["nxt"] = dst, src
@@ -249,7 +252,7 @@ def run(name, steps, warmup, with_cpu):
         "config": {
             "workload": name, "shard_elements": S, "world": w.world, "rank": w.rank,
             "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype, "buckets": plan.num_buckets,
-            "clip": clip, "algorithmic_bytes_per_element": bpe_total,
+            "clip": clip, "state_layout": "tiled", "algorithmic_bytes_per_element": bpe_total,
             "step_GBps": bpe_total * S / (ms_step * 1e-3) / 1e9,
             "kernel_ms": {k: round(v[0], 5) for k, v in kernels.items()},
             "parallelism": "one rank of N (single GPU)",
@@ -260,7 +263,7 @@ def run(name, steps, warmup, with_cpu):
                      "traffic": traffic},
     }
     if with_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, slices, [x for x in state["cur"]], S)
+        out["cpu_baseline"] = cpu_baseline(w, slices, state["cur"][0], S)
     del slices, A, B, gather
     torch.cuda.empty_cache()
     return out

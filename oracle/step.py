@@ -175,7 +175,8 @@ def shard_step(slices: Sequence[np.ndarray], grad_kind: str, param_kind: str, wo
         q = sumsq(g)
         c32 = clip_coefficient(q + other_sumsq, max_norm) if clip_override is None \
             else F32(clip_override)
-        g_used = np.multiply(g, c32, dtype=np.float32)
+        with np.errstate(invalid="ignore", over="ignore"):   # inf * 0 when the norm is inf
+            g_used = np.multiply(g, c32, dtype=np.float32)
     if flag:
         return StepResult(master.copy(), m.copy(), v.copy(), casts.narrow(master, param_kind),
                           True, g, q, c32)

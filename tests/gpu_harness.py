@@ -10,6 +10,7 @@ import torch
 
 import workloads as W
 import zero_sharded_mixed_plan_amd as Z
+from zero_sharded_mixed_plan_amd.optim import pack_state, state_arg_dict, unpack_state
 from oracle import casts as OC
 from oracle import plan as OP
 from oracle import step as OS
@@ -115,7 +116,8 @@ def compare_step(gpu_p, gpu_m, gpu_v, res: OS.StepResult, p_in, m_in, v_in, g_us
 class Rig:
     """Device buffers of one rank for workload w (inputs drawn on the CPU)."""
 
-    def __init__(self, w: W.Workload, ld_align: int = 64, device="cuda", rank=None):
+    def __init__(self, w: W.Workload, ld_align: int = 64, device="cuda", rank=None,
+                 layout: int = Z.ZERO_STATE_SEPARATE):
         if rank is not None:
             import dataclasses
             w = dataclasses.replace(w, rank=rank)
@@ -128,8 +130,14 @@ class Rig:
         self.dev = dev
         master, m, v = W.make_state(w, self.lay, "cpu")
         self.p0, self.m0, self.v0 = master.numpy().copy(), m.numpy().copy(), v.numpy().copy()
-        self.A = [x.to(dev) for x in (master, m, v)]
-        self.B = [torch.zeros(self.S, dtype=torch.float32, device=dev) for _ in range(3)]
+        self.layout = layout
+        if layout == Z.ZERO_STATE_TILED:
+            n = self.plan.state_numel(layout)
+            self.A = [pack_state(master.to(dev), m.to(dev), v.to(dev), n)]
+            self.B = [torch.zeros(n, dtype=torch.float32, device=dev)]
+        else:
+            self.A = [x.to(dev) for x in (master, m, v)]
+            self.B = [torch.zeros(self.S, dtype=torch.float32, device=dev) for _ in range(3)]
         # gather buffer: a random bit pattern everywhere (to catch stray writes),
         # the rank's pieces hold the rounded initial master
         rng = np.random.default_rng(w.seed + 1)
@@ -157,14 +165,20 @@ class Rig:
                     lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                     weight_decay=w.weight_decay, step=t)
 
+    def state_args(self, src, dst):
+        return state_arg_dict(self.layout, src, dst)
+
+    def unpack(self, bufs):
+        """(master, m, v) of a state buffer list as numpy [S] arrays."""
+        if self.layout == Z.ZERO_STATE_TILED:
+            return tuple(x.cpu().numpy() for x in unpack_state(bufs[0], self.S))
+        return tuple(x.cpu().numpy() for x in bufs)
+
     def fused(self, sl_dev, src, dst, t, overflow=True, skip=None):
         a = Z.adam_args(grad=sl_dev.data_ptr(), grad_ld=self.ld, grad_dtype=CODE[self.w.grad_dtype],
                         inv_scale=1.0 / self.w.loss_scale,
-                        master_in=src[0].data_ptr(), m_in=src[1].data_ptr(), v_in=src[2].data_ptr(),
-                        master_out=dst[0].data_ptr(), m_out=dst[1].data_ptr(),
-                        v_out=dst[2].data_ptr(),
                         overflow_out=self.flag.data_ptr() if overflow else None,
-                        skip_in=skip, **self.common(t))
+                        skip_in=skip, **self.state_args(src, dst), **self.common(t))
         Z.zero_adam_step(self.plan, a, torch.cuda.current_stream().cuda_stream)
 
     def reduce_norm(self, sl_dev, other=0.0, max_norm=None):
@@ -175,12 +189,10 @@ class Rig:
                           self.w.max_norm if max_norm is None else max_norm, self.flag.data_ptr(),
                           self.sumsq.data_ptr(), self.clip.data_ptr(), st)
 
-    def stash_step(self, state, t):
+    def stash_step(self, state, t, skip=True):
         a = Z.adam_args(g_stash=self.g.data_ptr(), clip_coef=self.clip.data_ptr(),
-                        master_in=state[0].data_ptr(), m_in=state[1].data_ptr(),
-                        v_in=state[2].data_ptr(), master_out=state[0].data_ptr(),
-                        m_out=state[1].data_ptr(), v_out=state[2].data_ptr(),
-                        skip_in=self.flag.data_ptr(), **self.common(t))
+                        skip_in=self.flag.data_ptr() if skip is True else skip,
+                        **self.state_args(state, state), **self.common(t))
         Z.zero_adam_step(self.plan, a, torch.cuda.current_stream().cuda_stream)
 
     def gather_np(self):

@@ -150,3 +150,24 @@ def test_reduce_and_norm_validation():
     with pytest.raises(Z.ZeroError) as e:
         Z.zero_shard_norm(plan, BASE, 0.0, float("inf"), 0, 0, 0)
     assert e.value.code == Z.ZERO_EINVAL
+
+
+def test_state_numel():
+    p = Z.Plan([10_000], 4)          # S = 2500 -> 2 tiles of 2048
+    assert p.state_numel(Z.ZERO_STATE_SEPARATE) == 2500
+    assert p.state_numel(Z.ZERO_STATE_TILED) == 2 * 3 * 2048
+    with pytest.raises(Z.ZeroError):
+        p.state_numel(7)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(state_layout=1), Z.ZERO_EINVAL),                       # tiled takes master only
+    (dict(state_layout=1, m_in=None, v_in=None, m_out=None, v_out=None,
+          master_out=BASE + (1 << 32) + 4096), Z.ZERO_EINVAL),   # in/out buffers overlap
+    (dict(state_layout=3), Z.ZERO_EINVAL),                       # unknown layout
+])
+def test_tiled_state_validation(over, code):
+    plan = Z.Plan(W.numels(W.toy_mlp()), 4)
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_adam_step(plan, _good(plan, **over))
+    assert e.value.code == code, Z.zero_last_error()

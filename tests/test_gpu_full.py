@@ -1,7 +1,8 @@
 """GPU parity at the five workloads' full sizes, in the launch configuration the
 benchmark times (slice stride rounded up to 64 elements, one-shot grids).
 
-The step is elementwise, so the oracle computes sampled elements one by one:
+The optimizer state uses the benchmark's tiled layout.  The step is
+elementwise, so the oracle computes sampled elements one by one:
 2^18 random local indices plus every piece boundary and the shard's ends.
 Properties that hold at any size cover the rest: the gather buffer outside the
 rank's pieces is untouched, the overflow flag is exact, and the norm equals a
@@ -14,6 +15,7 @@ import torch
 import workloads as W
 import zero_sharded_mixed_plan_amd as Z
 from gpu_harness import CODE, check_params, compare_step, oracle_layout, say, storage
+from zero_sharded_mixed_plan_amd.optim import pack_state, state_arg_dict
 from oracle import casts as OC
 from oracle import step as OS
 
@@ -55,8 +57,12 @@ def test_full_size(name):
     assert plan.shard_numel == S and plan.segments(w.rank) == lay.segments
     ld = (S + 63) // 64 * 64
     say(f"full {name}: S={S} N={w.world} rank={w.rank} pieces={len(lay.segments)} ld={ld}")
-    A = list(W.make_state(w, lay, dev))
-    B = [torch.empty_like(x) for x in A]
+    # the benchmark's state layout: tiles of master|m|v
+    layout, T = Z.ZERO_STATE_TILED, Z.ZERO_STATE_TILE
+    p0, m0, v0 = W.make_state(w, lay, dev)
+    A = [pack_state(p0, m0, v0, plan.state_numel(layout))]
+    del p0, m0, v0
+    B = [torch.empty_like(A[0])]
     pdt = W.torch_dtype(w.param_dtype)
     gather = torch.full((pl.padded_numel,), SENTINEL[w.param_dtype], dtype=pdt, device=dev)
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -74,6 +80,11 @@ def test_full_size(name):
         sel = (idx >= lo) & (idx < lo + ln)
         gidx[sel] = idx[sel] - lo + goff
     gidx_dev = torch.from_numpy(gidx).to(dev)
+    soff = (idx // T) * 3 * T + idx % T
+    soff_dev = [torch.from_numpy(soff + i * T).to(dev) for i in range(3)]
+
+    def take_state(bufs):
+        return tuple(_take(bufs[0], soff_dev[i]) for i in range(3))
     st = torch.cuda.current_stream().cuda_stream
     cur, nxt = A, B
     t = w.t0
@@ -81,7 +92,7 @@ def test_full_size(name):
     steps = 3 if w.inject_inf_step is not None else 1
     for step in range(1, steps + 1):
         slices = W.make_slices(w, lay, step=step, ld=ld, device=dev, out=slices)
-        p_in, m_in, v_in = (_take(x, idx_dev) for x in cur)
+        p_in, m_in, v_in = take_state(cur)
         sl = [_take(slices[k, :S], idx_dev) for k in range(w.world)]
         common = dict(rank=w.rank, gather=gather.data_ptr(), param_dtype=CODE[w.param_dtype],
                       lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
@@ -93,10 +104,8 @@ def test_full_size(name):
                                 g.data_ptr(), ws.data_ptr(), True, st)
             Z.zero_shard_norm(plan, ws.data_ptr(), 0.0, w.max_norm, flag.data_ptr(),
                               sumsq.data_ptr(), coef.data_ptr(), st)
-            p, m, v = cur
-            a = Z.adam_args(g_stash=g.data_ptr(), clip_coef=coef.data_ptr(), master_in=p.data_ptr(),
-                            m_in=m.data_ptr(), v_in=v.data_ptr(), master_out=p.data_ptr(),
-                            m_out=m.data_ptr(), v_out=v.data_ptr(), skip_in=flag.data_ptr(), **common)
+            a = Z.adam_args(g_stash=g.data_ptr(), clip_coef=coef.data_ptr(), skip_in=flag.data_ptr(),
+                            **state_arg_dict(layout, cur, cur), **common)
             Z.zero_adam_step(plan, a, st)
             torch.cuda.synchronize()
             q = float(sumsq.item())
@@ -111,10 +120,8 @@ def test_full_size(name):
             say(f"  q={q:.6g} norm={np.sqrt(q):.6g} clip={float(c32):.6g}")
         else:
             a = Z.adam_args(grad=slices.data_ptr(), grad_ld=ld, grad_dtype=CODE[w.grad_dtype],
-                            inv_scale=1.0 / w.loss_scale, master_in=cur[0].data_ptr(),
-                            m_in=cur[1].data_ptr(), v_in=cur[2].data_ptr(),
-                            master_out=nxt[0].data_ptr(), m_out=nxt[1].data_ptr(),
-                            v_out=nxt[2].data_ptr(), overflow_out=flag.data_ptr(), **common)
+                            inv_scale=1.0 / w.loss_scale, overflow_out=flag.data_ptr(),
+                            **state_arg_dict(layout, cur, nxt), **common)
             Z.zero_adam_step(plan, a, st)
             torch.cuda.synchronize()
             res = OS.shard_step(sl, w.grad_dtype, w.param_dtype, w.world, p_in, m_in, v_in, **kw)
@@ -125,7 +132,7 @@ def test_full_size(name):
         if not clip:
             # a sample may miss the injected element: the flag is decided on the whole shard
             out = cur if flag_gpu else nxt
-        gp, gm, gv = (_take(x, idx_dev) for x in out)
+        gp, gm, gv = take_state(out)
         if injected:
             for a_, b_ in ((gp, p_in), (gm, m_in), (gv, v_in)):
                 assert np.array_equal(a_.view(np.uint32), b_.view(np.uint32))

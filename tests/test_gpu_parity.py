@@ -28,12 +28,16 @@ def _oracle_slices(sl_cpu, S, world):
     return [storage(sl_cpu[k, :S]) for k in range(world)]
 
 
-def run_workload(w: W.Workload, ld_align=64, rank=None, steps=None):
+SEP, TILED = Z.ZERO_STATE_SEPARATE, Z.ZERO_STATE_TILED
+LAYOUTS = pytest.mark.parametrize("layout", [SEP, TILED], ids=["separate", "tiled"])
+
+
+def run_workload(w: W.Workload, ld_align=64, rank=None, steps=None, layout=SEP):
     """Run w.steps steps on the GPU and in the oracle; compare everything."""
-    rig = Rig(w, ld_align=ld_align, rank=rank)
+    rig = Rig(w, ld_align=ld_align, rank=rank, layout=layout)
     w = rig.w
     say(f"workload {w.name} S={rig.S} N={w.world} rank={w.rank} grads={w.grad_dtype} "
-        f"params={w.param_dtype} buckets={len(rig.lay.segments)} ld={rig.ld}")
+        f"params={w.param_dtype} buckets={len(rig.lay.segments)} ld={rig.ld} layout={layout}")
     p, m, v = rig.p0, rig.m0, rig.v0
     gather_ref = rig.gather0.copy()
     cur, nxt = rig.A, rig.B
@@ -69,7 +73,7 @@ def run_workload(w: W.Workload, ld_align=64, rank=None, steps=None):
         torch.cuda.synchronize()
         flag = int(rig.flag.item())
         assert flag == int(res.flag), f"step {step}: flag {flag} vs oracle {res.flag}"
-        gp, gm, gv = (x.cpu().numpy() for x in out)
+        gp, gm, gv = rig.unpack(out)
         g_used = res.g if w.max_norm <= 0 else np.multiply(res.g, res.clip, dtype=F)
         n, tot = compare_step(gp, gm, gv, res, p, m, v, g_used,
                               OS.adam_consts(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t + 1),
@@ -93,9 +97,10 @@ def run_workload(w: W.Workload, ld_align=64, rank=None, steps=None):
     return rig
 
 
+@LAYOUTS
 @pytest.mark.parametrize("name", W.ORDER)
-def test_small_workloads(name):
-    run_workload(W.SMALL[name])
+def test_small_workloads(name, layout):
+    run_workload(W.SMALL[name], layout=layout)
 
 
 def test_toy_all_ranks_union_equals_unsharded():
@@ -135,6 +140,8 @@ def _flat(psi, world, rank, g, p, seed=3, **kw):
 @pytest.mark.parametrize("p", ["f32", "bf16", "f16"])
 def test_dtype_matrix(g, p):
     run_workload(_flat(4 * 5003, 4, 3, g, p))
+    if g == p:
+        run_workload(_flat(4 * 5003, 4, 3, g, p), layout=TILED)
 
 
 @pytest.mark.parametrize("world,rank,psi", [
@@ -150,6 +157,7 @@ def test_dtype_matrix(g, p):
 ])
 def test_world_and_alignment(world, rank, psi):
     run_workload(_flat(psi, world, rank, "bf16", "bf16"))
+    run_workload(_flat(psi, world, rank, "bf16", "bf16"), layout=TILED)
 
 
 def test_loss_scaled_fp16():
@@ -169,16 +177,18 @@ def test_many_buckets_several_launches():
                    lr=1e-3, weight_decay=0.1, steps=2, seed=9)
     pl = OP.make_plan(sizes, 3, 150)
     assert len(pl.buckets) > 60
-    run_workload(w)
-    run_workload(dataclasses.replace(w, max_norm=1e-3, name="many_buckets_clip"))
+    for layout in (SEP, TILED):
+        run_workload(w, layout=layout)
+        run_workload(dataclasses.replace(w, max_norm=1e-3, name="many_buckets_clip"), layout=layout)
 
 
+@LAYOUTS
 @pytest.mark.parametrize("bad", ["+inf", "-inf", "nan", "f16_overflow"])
 @pytest.mark.parametrize("mode", ["fused", "stash"])
-def test_overflow_skips_bitwise(bad, mode):
+def test_overflow_skips_bitwise(bad, mode, layout):
     gk = "f16" if bad == "f16_overflow" else "bf16"
     w = _flat(8 * 3001, 8, 5, gk, gk, max_norm=(1.0 if mode == "stash" else 0.0))
-    rig = Rig(w)
+    rig = Rig(w, layout=layout)
     say(f"overflow {bad} {mode}")
     sl_cpu, _ = rig.slices(1)
     val = {"+inf": float("inf"), "-inf": float("-inf"), "nan": float("nan"),
@@ -199,43 +209,40 @@ def test_overflow_skips_bitwise(bad, mode):
     assert np.array_equal(rig.gather_np(), rig.gather0)
 
 
+@LAYOUTS
 @pytest.mark.parametrize("mode", ["fused", "stash"])
-def test_forced_skip(mode):
+def test_forced_skip(mode, layout):
     w = _flat(4 * 2000, 4, 2, "bf16", "bf16", max_norm=(1.0 if mode == "stash" else 0.0))
-    rig = Rig(w)
+    rig = Rig(w, layout=layout)
     _, sl_dev = rig.slices(1)
     skip = torch.ones(1, dtype=torch.int32, device="cuda")
     before = [x.clone() for x in rig.A]
     if mode == "fused":
-        rig.B[1].fill_(3.0)
+        rig.B[-1].fill_(3.0)
         rig.fused(sl_dev, rig.A, rig.B, 1, skip=skip.data_ptr())
         torch.cuda.synchronize()
         assert rig.flag.item() == 1
-        assert torch.all(rig.B[1] == 3.0)
+        assert torch.all(rig.B[-1] == 3.0)
     else:
         rig.reduce_norm(sl_dev)
-        a = Z.adam_args(g_stash=rig.g.data_ptr(), clip_coef=rig.clip.data_ptr(),
-                        master_in=rig.A[0].data_ptr(), m_in=rig.A[1].data_ptr(),
-                        v_in=rig.A[2].data_ptr(), master_out=rig.A[0].data_ptr(),
-                        m_out=rig.A[1].data_ptr(), v_out=rig.A[2].data_ptr(),
-                        skip_in=skip.data_ptr(), **rig.common(1))
-        Z.zero_adam_step(rig.plan, a, torch.cuda.current_stream().cuda_stream)
+        rig.stash_step(rig.A, 1, skip=skip.data_ptr())
         torch.cuda.synchronize()
     for a, b in zip(rig.A, before):
         assert torch.equal(a, b)
     assert np.array_equal(rig.gather_np(), rig.gather0)
 
 
-def test_no_flag_in_place_matches():
+@LAYOUTS
+def test_no_flag_in_place_matches(layout):
     """Fused step without an overflow flag, updated in place."""
     w = _flat(4 * 3000 + 3, 4, 3, "bf16", "bf16")
-    rig = Rig(w)
+    rig = Rig(w, layout=layout)
     sl_cpu, sl_dev = rig.slices(1)
     rig.fused(sl_dev, rig.A, rig.A, 1, overflow=False)
     torch.cuda.synchronize()
     res = OS.shard_step([storage(sl_cpu[k, :rig.S]) for k in range(4)], "bf16", "bf16", 4,
                         rig.p0, rig.m0, rig.v0, lr=w.lr, weight_decay=w.weight_decay, t=1)
-    assert np.array_equal(rig.A[0].cpu().numpy().view(np.uint32), res.master.view(np.uint32))
+    assert np.array_equal(rig.unpack(rig.A)[0].view(np.uint32), res.master.view(np.uint32))
 
 
 def test_norm_deterministic_and_partitioned():

@@ -2,19 +2,20 @@
 
 The computation runs in libzero_shard.so (hand-written HIP kernels for gfx950
 behind a C ABI, include/zero_shard.h); this package is its thin Python binding
-plus a small optimizer object over torch device tensors.  Importing it loads the
-library and fails loudly if it has not been built.
+plus a small optimizer object over torch device tensors.  The library is loaded
+on first use (any planner or device call), which fails loudly if it has not been
+built; nothing here falls back to another implementation.
 """
 from ._abi import (DTYPE_BYTES, DTYPE_CODES, EXPORTS, ZERO_BF16, ZERO_EALIGN, ZERO_EHIP,
-                   ZERO_EINVAL, ZERO_ENOMEM, ZERO_F16, ZERO_F32, ZERO_OK, Plan, ZeroError,
+                   ZERO_EINVAL, ZERO_ENOMEM, ZERO_F16, ZERO_F32, ZERO_OK, ZERO_STATE_SEPARATE,
+                   ZERO_STATE_TILE, ZERO_STATE_TILED, Plan, ZeroError,
                    adam_args, lib, zero_adam_args_t, zero_adam_step, zero_last_error,
                    zero_reduce_shard, zero_shard_norm, zero_version)
 
-lib()
-
 __all__ = [
     "DTYPE_BYTES", "DTYPE_CODES", "EXPORTS", "ZERO_BF16", "ZERO_EALIGN", "ZERO_EHIP", "ZERO_EINVAL",
-    "ZERO_ENOMEM", "ZERO_F16", "ZERO_F32", "ZERO_OK", "Plan", "ZeroError", "adam_args", "lib",
+    "ZERO_ENOMEM", "ZERO_F16", "ZERO_F32", "ZERO_OK", "ZERO_STATE_SEPARATE", "ZERO_STATE_TILE",
+    "ZERO_STATE_TILED", "Plan", "ZeroError", "adam_args", "lib",
     "zero_adam_args_t", "zero_adam_step", "zero_last_error", "zero_reduce_shard",
     "zero_shard_norm", "zero_version",
 ]

@@ -16,6 +16,8 @@ LIB_PATH = os.environ.get("ZERO_SHARD_LIB") or os.path.join(
 
 ZERO_OK, ZERO_EINVAL, ZERO_EALIGN, ZERO_ENOMEM, ZERO_EHIP = 0, -1, -2, -3, -4
 ZERO_F32, ZERO_BF16, ZERO_F16 = 0, 1, 2
+ZERO_STATE_SEPARATE, ZERO_STATE_TILED = 0, 1
+ZERO_STATE_TILE = 2048
 DTYPE_CODES = {"f32": ZERO_F32, "bf16": ZERO_BF16, "f16": ZERO_F16}
 DTYPE_BYTES = {ZERO_F32: 4, ZERO_BF16: 2, ZERO_F16: 2}
 
@@ -24,7 +26,7 @@ EXPORTS = [
     "zero_plan", "zero_plan_free", "zero_plan_shard_numel", "zero_plan_total_numel",
     "zero_plan_padded_numel", "zero_plan_world", "zero_plan_num_buckets", "zero_plan_num_tensors",
     "zero_plan_bucket", "zero_plan_tensor", "zero_plan_rank_segment", "zero_plan_bytes",
-    "zero_workspace_bytes", "zero_reduce_shard", "zero_shard_norm", "zero_adam_step",
+    "zero_state_numel", "zero_workspace_bytes", "zero_reduce_shard", "zero_shard_norm", "zero_adam_step",
     "zero_last_error", "zero_version",
 ]
 
@@ -44,6 +46,7 @@ class zero_adam_args_t(ctypes.Structure):
         ("inv_scale", ctypes.c_float),
         ("g_stash", ctypes.c_void_p),
         ("clip_coef", ctypes.c_void_p),
+        ("state_layout", ctypes.c_int32),
         ("master_in", ctypes.c_void_p),
         ("m_in", ctypes.c_void_p),
         ("v_in", ctypes.c_void_p),
@@ -100,6 +103,7 @@ def load(path: str) -> ctypes.CDLL:
         "zero_plan_tensor": (ctypes.c_int, [vp, i32, P32, P64]),
         "zero_plan_rank_segment": (ctypes.c_int, [vp, i32, i32, P64, P64, P64]),
         "zero_plan_bytes": (ctypes.c_int, [vp, i32, ctypes.POINTER(f64), P64]),
+        "zero_state_numel": (i64, [vp, i32]),
         "zero_workspace_bytes": (ctypes.c_size_t, [vp]),
         "zero_reduce_shard": (ctypes.c_int, [vp, vp, i64, ctypes.c_int, f32, vp, vp, i32, vp]),
         "zero_shard_norm": (ctypes.c_int, [vp, vp, f64, f64, vp, vp, vp, vp]),
@@ -215,6 +219,12 @@ class Plan:
 
     def workspace_bytes(self) -> int:
         return lib().zero_workspace_bytes(self.handle)
+
+    def state_numel(self, layout: int) -> int:
+        n = lib().zero_state_numel(self.handle, layout)
+        if n < 0:
+            raise ZeroError(ZERO_EINVAL, "unknown state layout")
+        return n
 
 
 # ---------------------------------------------------------------------------

@@ -136,10 +136,19 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
   const int pb = dtype_bytes(A.param_dtype);
   if (pb == 0) return fail(ZERO_EINVAL, "zero_adam_step: unsupported parameter dtype");
 
-  // pointers and alignment
+  // state pointers and alignment
+  const bool tiled = A.state_layout == ZERO_STATE_TILED;
+  if (A.state_layout != ZERO_STATE_SEPARATE && !tiled)
+    return fail(ZERO_EINVAL, "zero_adam_step: unknown state layout");
   const float* ins[3] = {A.master_in, A.m_in, A.v_in};
   float* outs[3] = {A.master_out, A.m_out, A.v_out};
+  const int n_arrays = tiled ? 1 : 3;
   for (int i = 0; i < 3; ++i) {
+    if (i >= n_arrays) {
+      if (ins[i] || outs[i])
+        return fail(ZERO_EINVAL, "zero_adam_step: the tiled state layout takes master_in/master_out only");
+      continue;
+    }
     if (!ins[i] || !outs[i]) return fail(ZERO_EINVAL, "zero_adam_step: state pointer is NULL");
     if (!aligned(ins[i], 16) || !aligned(outs[i], 16))
       return fail(ZERO_EALIGN, "zero_adam_step: state arrays must be 16-byte aligned");
@@ -167,25 +176,26 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
   // aliasing: outputs never overlap each other or the gather buffer; in the
   // fused step with an overflow flag they must not overlap any input either
   // (the inputs are what a skipped step keeps)
-  const int64_t sb = S * 4;
-  std::vector<Range> out_r = {rng(A.master_out, sb, "master_out"), rng(A.m_out, sb, "m_out"),
-                              rng(A.v_out, sb, "v_out"),
-                              rng(A.gather, plan->padded * pb, "gather")};
+  const int64_t sb = (tiled ? zero_state_numel(plan, ZERO_STATE_TILED) : S) * 4;
+  static const char* in_names[3] = {"master_in", "m_in", "v_in"};
+  static const char* out_names[3] = {"master_out", "m_out", "v_out"};
+  std::vector<Range> out_r, in_r;
+  for (int i = 0; i < n_arrays; ++i) out_r.push_back(rng(outs[i], sb, out_names[i]));
+  out_r.push_back(rng(A.gather, plan->padded * pb, "gather"));
   for (size_t i = 0; i < out_r.size(); ++i)
     for (size_t j = i + 1; j < out_r.size(); ++j)
       if (overlaps(out_r[i], out_r[j]))
         return fail(ZERO_EINVAL, std::string("zero_adam_step: ") + out_r[i].name + " overlaps " + out_r[j].name);
-  std::vector<Range> in_r = {rng(A.master_in, sb, "master_in"), rng(A.m_in, sb, "m_in"),
-                             rng(A.v_in, sb, "v_in")};
+  for (int i = 0; i < n_arrays; ++i) in_r.push_back(rng(ins[i], sb, in_names[i]));
   if (stash)
-    in_r.push_back(rng(A.g_stash, sb, "g_stash"));
+    in_r.push_back(rng(A.g_stash, S * 4, "g_stash"));
   else
     in_r.push_back(rng(A.grad, ((int64_t)(N - 1) * A.grad_ld + S) * dtype_bytes(A.grad_dtype), "grad"));
   const bool strict = !stash && A.overflow_out != nullptr;
   for (size_t i = 0; i < in_r.size(); ++i) {
     for (size_t j = 0; j < out_r.size(); ++j) {
       if (!overlaps(in_r[i], out_r[j])) continue;
-      const bool same = (i < 3 && j == i && in_r[i].lo == out_r[j].lo);  // exact in-place update
+      const bool same = ((int)i < n_arrays && j == i && in_r[i].lo == out_r[j].lo);  // exact in-place update
       if (strict || !same)
         return fail(ZERO_EINVAL, std::string("zero_adam_step: ") + in_r[i].name + " overlaps " + out_r[j].name +
                                      (strict ? " (a fused step with an overflow flag needs separate output state)" : ""));
@@ -213,12 +223,27 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
   L.inv_scale = A.inv_scale;
   L.g_stash = A.g_stash;
   L.clip = A.clip_coef;
-  L.p_in = A.master_in;
-  L.m_in = A.m_in;
-  L.v_in = A.v_in;
-  L.p_out = A.master_out;
-  L.m_out = A.m_out;
-  L.v_out = A.v_out;
+  if (tiled) {
+    L.p_in = A.master_in;
+    L.m_in = A.master_in + zk::kStateTile;
+    L.v_in = A.master_in + 2 * zk::kStateTile;
+    L.p_out = A.master_out;
+    L.m_out = A.master_out + zk::kStateTile;
+    L.v_out = A.master_out + 2 * zk::kStateTile;
+    L.st_shift = zk::kStateTileShift;
+    L.st_mask = zk::kStateTile - 1;
+    L.st_stride = 3 * zk::kStateTile;
+  } else {
+    L.p_in = A.master_in;
+    L.m_in = A.m_in;
+    L.v_in = A.v_in;
+    L.p_out = A.master_out;
+    L.m_out = A.m_out;
+    L.v_out = A.v_out;
+    L.st_shift = 62;  // j >> 62 == 0 for every shard index: plain j
+    L.st_mask = -1;
+    L.st_stride = 0;
+  }
   L.gather = static_cast<char*>(A.gather);
   L.skip_in = A.skip_in;
   L.overflow = stash ? nullptr : A.overflow_out;

@@ -181,6 +181,13 @@ __device__ __forceinline__ void st8(float* p, const float o[8]) {
   reinterpret_cast<float4*>(p)[1] = make_float4(o[4], o[5], o[6], o[7]);
 }
 
+// the fp32 gradient stash of the clipped path is written once here and read once
+// by the update kernel; streaming it past the caches measured 2% faster
+__device__ __forceinline__ void st8_stream(float* p, const float o[8]) {
+  st_stream16(p, make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])));
+  st_stream16(p + 4, make_uint4(__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])));
+}
+
 // ---------------------------------------------------------------------------
 // the arithmetic of one element (shared by all paths of all kernels)
 // ---------------------------------------------------------------------------
@@ -257,6 +264,14 @@ __device__ __forceinline__ float reduce1(const char* base, int64_t ld_bytes, int
 template <class T, bool WIDE> struct Batch { static constexpr int value = WIDE ? 16 : 8; };
 template <bool WIDE> struct Batch<TF32, WIDE> { static constexpr int value = WIDE ? 8 : 4; };
 
+// Offset of local element j in the state arrays.  Separate [S] arrays: j.
+// Tiled state (one buffer, tiles of master|m|v of kStateTile elements each):
+// (j / tile) * 3 * tile + j % tile, with the m and v bases one and two tiles on.
+// A vector of 8 never straddles a tile.
+__device__ __forceinline__ int64_t state_off(const StepLaunch& a, int64_t j) {
+  return (j >> a.st_shift) * a.st_stride + (j & a.st_mask);
+}
+
 // gather index offset of local element j (uniform loop over the launch's pieces)
 __device__ __forceinline__ int64_t delta_of(const StepLaunch& a, int64_t j) {
   int64_t d = a.seg[0].delta;
@@ -286,9 +301,10 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
   float p[8], m[8], s[8], g[8];
   bool bad = false;
   if (j0 + kVec <= a.S) {
-    ld8(a.p_in + j0, p);
-    ld8(a.m_in + j0, m);
-    ld8(a.v_in + j0, s);
+    const int64_t o0 = state_off(a, j0);
+    ld8(a.p_in + o0, p);
+    ld8(a.m_in + o0, m);
+    ld8(a.v_in + o0, s);
     if (STASH) {
       ld8(a.g_stash + j0, g);
 #pragma unroll
@@ -305,9 +321,9 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) adamw1(p[e], m[e], s[e], g[e], a.c);
-    st8(a.p_out + j0, p);
-    st8(a.m_out + j0, m);
-    st8(a.v_out + j0, s);
+    st8(a.p_out + o0, p);
+    st8(a.m_out + o0, m);
+    st8(a.v_out + o0, s);
     const int64_t d0 = delta_of(a, j0);
     if (delta_of(a, j0 + kVec - 1) == d0) {
       store_params8<PT>(a.gather + (j0 + d0) * PT::bytes, p);
@@ -320,7 +336,8 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
     for (int e = 0; e < 8; ++e) {
       const int64_t j = j0 + e;
       if (j >= a.S) break;
-      float pe = a.p_in[j], me = a.m_in[j], ve = a.v_in[j], ge;
+      const int64_t oj = state_off(a, j);
+      float pe = a.p_in[oj], me = a.m_in[oj], ve = a.v_in[oj], ge;
       if (STASH) {
         ge = a.g_stash[j] * clip;
       } else {
@@ -329,9 +346,9 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
         bad |= !__builtin_isfinite(ge);
       }
       adamw1(pe, me, ve, ge, a.c);
-      a.p_out[j] = pe;
-      a.m_out[j] = me;
-      a.v_out[j] = ve;
+      a.p_out[oj] = pe;
+      a.m_out[oj] = me;
+      a.v_out[oj] = ve;
       store_param1<PT>(a.gather + (j + delta_of(a, j)) * PT::bytes, pe);
     }
   }
@@ -348,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void recast_kernel(const StepLaunch a, co
     const int64_t j0 = v * kVec;
     if (j0 + kVec <= a.S) {
       float p[8];
-      ld8(a.p_in + j0, p);
+      ld8(a.p_in + state_off(a, j0), p);
       const int64_t d0 = delta_of(a, j0);
       if (delta_of(a, j0 + kVec - 1) == d0) {
         store_params8<PT>(a.gather + (j0 + d0) * PT::bytes, p);
@@ -356,7 +373,8 @@ __global__ __launch_bounds__(kThreads) void recast_kernel(const StepLaunch a, co
         for (int e = 0; e < 8; ++e) store_param1<PT>(a.gather + (j0 + e + delta_of(a, j0 + e)) * PT::bytes, p[e]);
       }
     } else {
-      for (int64_t j = j0; j < a.S; ++j) store_param1<PT>(a.gather + (j + delta_of(a, j)) * PT::bytes, a.p_in[j]);
+      for (int64_t j = j0; j < a.S; ++j)
+        store_param1<PT>(a.gather + (j + delta_of(a, j)) * PT::bytes, a.p_in[state_off(a, j)]);
     }
   }
 }
@@ -389,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) 
         g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, a.inv_scale);
         bad |= !__builtin_isfinite(g[e]);
       }
-      if (a.g_out != nullptr) st8(a.g_out + j0, g);
+      if (a.g_out != nullptr) st8_stream(a.g_out + j0, g);
       if (a.want_sumsq) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) sq += (double)g[e] * (double)g[e];

@@ -152,4 +152,11 @@ extern "C" int zero_plan_bytes(const zero_plan_t* p, int32_t stage, double* form
   return ZERO_OK;
 }
 
+extern "C" int64_t zero_state_numel(const zero_plan_t* p, int32_t layout) {
+  if (!p) return -1;
+  if (layout == ZERO_STATE_SEPARATE) return p->shard;
+  if (layout == ZERO_STATE_TILED) return (p->shard + zk::kStateTile - 1) / zk::kStateTile * 3 * zk::kStateTile;
+  return -1;
+}
+
 extern "C" size_t zero_workspace_bytes(const zero_plan_t* p) { return p ? zk::ws_bytes(p->shard) : 0; }

@@ -33,6 +33,8 @@ constexpr int kVec = 8;         // elements per thread per tile
 constexpr int kTile = kThreads * kVec;
 constexpr int kMaxSeg = 24;     // gather pieces one launch of the update kernel can address
 constexpr int kNormThreads = 1024;    // the one-workgroup norm finalize
+constexpr int kStateTileShift = 11;   // tiled state: 2048 elements of master, m, v per tile
+constexpr int64_t kStateTile = int64_t(1) << kStateTileShift;
 constexpr int kStreamBlocksPerCU = 3; // resident workgroups per CU of the streaming kernels
 
 // A rank piece as seen by one launch: local elements [.., end) map to gather
@@ -64,6 +66,9 @@ struct StepLaunch {
   float* p_out;
   float* m_out;
   float* v_out;
+  int32_t st_shift;       // state addressing: (j >> st_shift) * st_stride + (j & st_mask)
+  int64_t st_mask;
+  int64_t st_stride;
   char* gather;
   AdamK c;
   const uint32_t* skip_in;

@@ -34,6 +34,37 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+def pack_state(master: torch.Tensor, m: torch.Tensor, v: torch.Tensor, numel: int) -> torch.Tensor:
+    """Three [S] fp32 arrays -> one tiled state buffer of `numel` elements
+    (tiles of ZERO_STATE_TILE master, then m, then v; the last tile zero-padded)."""
+    T = _abi.ZERO_STATE_TILE
+    nt = numel // (3 * T)
+    S = master.numel()
+    buf = torch.zeros(numel, dtype=torch.float32, device=master.device)
+    view = buf.view(nt, 3, T)
+    pad = torch.zeros(nt * T, dtype=torch.float32, device=master.device)
+    for i, x in enumerate((master, m, v)):
+        pad[:S].copy_(x)
+        view[:, i, :].copy_(pad.view(nt, T))
+    return buf
+
+
+def unpack_state(buf: torch.Tensor, S: int):
+    """Tiled state buffer -> (master, m, v) as [S] copies."""
+    T = _abi.ZERO_STATE_TILE
+    view = buf.view(-1, 3, T)
+    return tuple(view[:, i, :].reshape(-1)[:S].clone() for i in range(3))
+
+
+def state_arg_dict(layout: int, src, dst) -> dict:
+    """zero_adam_args_t state fields for lists of buffers (3 arrays, or 1 tiled buffer)."""
+    if layout == _abi.ZERO_STATE_TILED:
+        return dict(state_layout=layout, master_in=src[0].data_ptr(), master_out=dst[0].data_ptr())
+    return dict(state_layout=layout, master_in=src[0].data_ptr(), m_in=src[1].data_ptr(),
+                v_in=src[2].data_ptr(), master_out=dst[0].data_ptr(), m_out=dst[1].data_ptr(),
+                v_out=dst[2].data_ptr())
+
+
 class ZeroAdam:
     """Sharded AdamW state and step of rank `rank` out of `world`.
 
@@ -50,7 +81,8 @@ class ZeroAdam:
                  bucket_cap: int = 0, grad_dtype=torch.bfloat16, param_dtype=torch.bfloat16,
                  max_norm: float = 0.0, loss_scale: float = 1.0, dynamic_loss_scale: bool = False,
                  growth_interval: int = 2000, master: Optional[torch.Tensor] = None,
-                 gather: Optional[torch.Tensor] = None, device="cuda"):
+                 gather: Optional[torch.Tensor] = None, device="cuda",
+                 state_layout: int = _abi.ZERO_STATE_TILED):
         self.plan = _abi.Plan(numels, world, bucket_cap)
         self.world, self.rank = int(world), int(rank)
         self.lr, self.betas, self.eps, self.weight_decay = lr, tuple(betas), eps, weight_decay
@@ -67,10 +99,19 @@ class ZeroAdam:
         dev = torch.device(device)
         f32 = dict(dtype=torch.float32, device=dev)
         n_sets = 1 if self.max_norm > 0 else 2
-        self._state = [[torch.zeros(S, **f32) for _ in range(3)] for _ in range(n_sets)]
+        self.layout = state_layout
+        if state_layout == _abi.ZERO_STATE_TILED:
+            n = self.plan.state_numel(state_layout)
+            self._state = [[torch.zeros(n, **f32)] for _ in range(n_sets)]
+        else:
+            self._state = [[torch.zeros(S, **f32) for _ in range(3)] for _ in range(n_sets)]
         self._cur = 0
         if master is not None:
-            self._state[0][0].copy_(master)
+            if state_layout == _abi.ZERO_STATE_TILED:
+                z = torch.zeros(S, **f32)
+                self._state[0][0].copy_(pack_state(master.to(**f32), z, z, self._state[0][0].numel()))
+            else:
+                self._state[0][0].copy_(master)
         self.gather = gather if gather is not None else torch.zeros(
             self.plan.padded_numel, dtype=param_dtype, device=dev)
         if self.gather.numel() != self.plan.padded_numel or self.gather.dtype != param_dtype:
@@ -83,17 +124,24 @@ class ZeroAdam:
             self.clip = torch.ones(1, **f32)
 
     # -- state ---------------------------------------------------------------
+    def state(self):
+        """(master, m, v) of this rank as [S] tensors (copies for the tiled layout)."""
+        cur = self._state[self._cur]
+        if self.layout == _abi.ZERO_STATE_TILED:
+            return unpack_state(cur[0], self.S)
+        return tuple(cur)
+
     @property
     def master(self) -> torch.Tensor:
-        return self._state[self._cur][0]
+        return self.state()[0]
 
     @property
     def m(self) -> torch.Tensor:
-        return self._state[self._cur][1]
+        return self.state()[1]
 
     @property
     def v(self) -> torch.Tensor:
-        return self._state[self._cur][2]
+        return self.state()[2]
 
     def state_bytes(self) -> int:
         """fp32 master + m + v of this rank (the handbook's state_bytes())."""
@@ -121,20 +169,17 @@ class ZeroAdam:
                                    self.g.data_ptr(), self.ws.data_ptr(), True, st)
             _abi.zero_shard_norm(self.plan, self.ws.data_ptr(), other_ranks_sumsq, self.max_norm,
                                  self.flag.data_ptr(), self.sumsq.data_ptr(), self.clip.data_ptr(), st)
-            p, m, v = self._state[0]
+            cur = self._state[0]
             args = _abi.adam_args(g_stash=self.g.data_ptr(), clip_coef=self.clip.data_ptr(),
-                                  master_in=p.data_ptr(), m_in=m.data_ptr(), v_in=v.data_ptr(),
-                                  master_out=p.data_ptr(), m_out=m.data_ptr(), v_out=v.data_ptr(),
-                                  skip_in=self.flag.data_ptr(), **common)
+                                  skip_in=self.flag.data_ptr(),
+                                  **state_arg_dict(self.layout, cur, cur), **common)
             _abi.zero_adam_step(self.plan, args, st)
             ok = int(self.flag.item()) == 0
         else:
             src, dst = self._state[self._cur], self._state[1 - self._cur]
             args = _abi.adam_args(grad=slices.data_ptr(), grad_ld=slices.stride(0), grad_dtype=gcode,
-                                  inv_scale=inv, master_in=src[0].data_ptr(), m_in=src[1].data_ptr(),
-                                  v_in=src[2].data_ptr(), master_out=dst[0].data_ptr(),
-                                  m_out=dst[1].data_ptr(), v_out=dst[2].data_ptr(),
-                                  overflow_out=self.flag.data_ptr(), **common)
+                                  inv_scale=inv, overflow_out=self.flag.data_ptr(),
+                                  **state_arg_dict(self.layout, src, dst), **common)
             _abi.zero_adam_step(self.plan, args, st)
             ok = int(self.flag.item()) == 0
             if ok:
