@@ -144,8 +144,8 @@ int64_t zero_state_numel(const zero_plan_t* plan, int32_t layout);
 /*
  * Bytes of device workspace that zero_reduce_shard / zero_shard_norm need: one
  * float64 partial sum and one overflow word per 2048 shard elements (about
- * 6 bytes per 1000 elements).  Caller-allocated, 16-byte aligned, no initial
- * content required.  0 for a NULL plan.
+ * 6 bytes per 1000 elements) plus 3 KiB for the finalize.  Caller-allocated,
+ * 16-byte aligned, no initial content required.  0 for a NULL plan.
  */
 size_t zero_workspace_bytes(const zero_plan_t* plan);
 
@@ -170,7 +170,9 @@ int zero_reduce_shard(const zero_plan_t* plan, const void* grad, int64_t grad_ld
                       int32_t want_sumsq, void* stream);
 
 /*
- * Second pass (one workgroup): finalize what zero_reduce_shard left in `ws`.
+ * Second pass: finalize what zero_reduce_shard left in `ws` (two small launches:
+ * 256 workgroups sum fixed ranges of the per-workgroup partials into `ws`, one
+ * workgroup sums those in index order).
  *   overflow_out (device u32): 1 if any g was non-finite, else 0.
  *   q = sum of the partial sums in a fixed order; Q = q + other_ranks_sumsq (the
  *   other ranks' share of the global sum, 0 on one rank); norm = sqrt(Q) (fp64).
@@ -179,7 +181,7 @@ int zero_reduce_shard(const zero_plan_t* plan, const void* grad, int64_t grad_ld
  *   max_norm > 0 and norm > max_norm, else 1.
  * Errors: ZERO_EINVAL, ZERO_EHIP.
  */
-int zero_shard_norm(const zero_plan_t* plan, const void* ws, double other_ranks_sumsq,
+int zero_shard_norm(const zero_plan_t* plan, void* ws, double other_ranks_sumsq,
                     double max_norm, uint32_t* overflow_out, double* sumsq_out,
                     float* clip_coef_out, void* stream);
 

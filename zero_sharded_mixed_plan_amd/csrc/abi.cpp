@@ -101,7 +101,7 @@ extern "C" int zero_reduce_shard(const zero_plan_t* plan, const void* grad, int6
   return zk::launch_reduce(a, grad_dtype, zk::reduce_blocks(S), stream);
 }
 
-extern "C" int zero_shard_norm(const zero_plan_t* plan, const void* ws, double other_ranks_sumsq,
+extern "C" int zero_shard_norm(const zero_plan_t* plan, void* ws, double other_ranks_sumsq,
                                double max_norm, uint32_t* overflow_out, double* sumsq_out,
                                float* clip_coef_out, void* stream) {
   if (!plan) return fail(ZERO_EINVAL, "zero_shard_norm: plan is NULL");
@@ -114,9 +114,13 @@ extern "C" int zero_shard_norm(const zero_plan_t* plan, const void* ws, double o
       (overflow_out && !aligned(overflow_out, 4)))
     return fail(ZERO_EALIGN, "zero_shard_norm: misaligned output");
   zk::NormLaunch a{};
-  a.ws_flags = reinterpret_cast<const uint32_t*>(static_cast<const char*>(ws) + zk::ws_flags_offset(plan->shard));
-  a.ws_sums = reinterpret_cast<const double*>(static_cast<const char*>(ws) + zk::ws_sums_offset());
+  char* wsb = static_cast<char*>(ws);
+  a.ws_flags = reinterpret_cast<const uint32_t*>(wsb + zk::ws_flags_offset(plan->shard));
+  a.ws_sums = reinterpret_cast<const double*>(wsb + zk::ws_sums_offset());
+  a.l2_sums = reinterpret_cast<double*>(wsb + zk::ws_l2_sums_offset());
+  a.l2_flags = reinterpret_cast<uint32_t*>(wsb + zk::ws_l2_flags_offset());
   a.nblocks = zk::reduce_blocks(plan->shard);
+  a.chunk = (a.nblocks + zk::kNormGroups - 1) / zk::kNormGroups;
   a.other_sumsq = other_ranks_sumsq;
   a.max_norm = max_norm;
   a.overflow_out = overflow_out;

@@ -446,15 +446,13 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) 
   }
 }
 
-// One workgroup: OR of the overflow words, fixed-order sum of the partials,
-// global norm and clip coefficient.
-__global__ __launch_bounds__(kNormThreads) void norm_kernel(const NormLaunch a) {
-  double s = 0.0;
-  u32 f = 0;
-  for (int64_t i = threadIdx.x; i < a.nblocks; i += kNormThreads) {
-    s += a.ws_sums[i];
-    f |= a.ws_flags[i];
-  }
+// Finalize, in two fixed-order levels so the sum is the same run to run.
+// Level 1: workgroup g of kNormGroups sums the per-workgroup partials in
+// [g * chunk, (g + 1) * chunk) (strided per thread, then an LDS tree) and ORs the
+// overflow words.  Level 2: one workgroup sums the kNormGroups level-1 results in
+// index order, takes the norm and the clip coefficient.  Two launches: the
+// kernel boundary makes level 1's results visible to every XCD.
+__device__ __forceinline__ void block_sum_or(double& s, u32& f) {
   __shared__ double s_sum[kNormThreads];
   __shared__ u32 s_f[kNormThreads];
   s_sum[threadIdx.x] = s;
@@ -467,11 +465,39 @@ __global__ __launch_bounds__(kNormThreads) void norm_kernel(const NormLaunch a) 
     }
     __syncthreads();
   }
+  s = s_sum[0];
+  f = s_f[0];
+}
+
+__global__ __launch_bounds__(kNormThreads) void norm_partial_kernel(const NormLaunch a) {
+  const int64_t lo = (int64_t)blockIdx.x * a.chunk;
+  const int64_t hi = lo + a.chunk < a.nblocks ? lo + a.chunk : a.nblocks;
+  double s = 0.0;
+  u32 f = 0;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kNormThreads) {
+    s += a.ws_sums[i];
+    f |= a.ws_flags[i];
+  }
+  block_sum_or(s, f);
   if (threadIdx.x == 0) {
-    const double q = s_sum[0];
+    a.l2_sums[blockIdx.x] = s;
+    a.l2_flags[blockIdx.x] = f;
+  }
+}
+
+__global__ __launch_bounds__(kNormThreads) void norm_final_kernel(const NormLaunch a) {
+  double s = 0.0;
+  u32 f = 0;
+  for (int i = threadIdx.x; i < kNormGroups; i += kNormThreads) {
+    s += a.l2_sums[i];
+    f |= a.l2_flags[i];
+  }
+  block_sum_or(s, f);
+  if (threadIdx.x == 0) {
+    const double q = s;
     const double norm = __builtin_sqrt(q + a.other_sumsq);
     const double c = (a.max_norm > 0.0 && norm > a.max_norm) ? a.max_norm / norm : 1.0;
-    if (a.overflow_out) *a.overflow_out = s_f[0] ? 1u : 0u;
+    if (a.overflow_out) *a.overflow_out = f ? 1u : 0u;
     if (a.sumsq_out) *a.sumsq_out = q;
     if (a.clip_out) *a.clip_out = (float)c;
   }
@@ -530,7 +556,8 @@ static size_t occupancy_lds(int per_cu) {
 
 template <class GT, bool STASH>
 static int dispatch_pt(const StepLaunch& a, zero_dtype_t pt, unsigned blocks, hipStream_t st) {
-  const size_t lds = occupancy_lds(kStreamBlocksPerCU);
+  // the stash-mode update moves four streams and wants one workgroup more per CU
+  const size_t lds = occupancy_lds(STASH ? kStashBlocksPerCU : kStreamBlocksPerCU);
   switch (pt) {
     case ZERO_F32: go_step<GT, TF32, STASH>(a, blocks, lds, st); return ZERO_OK;
     case ZERO_BF16: go_step<GT, TBF16, STASH>(a, blocks, lds, st); return ZERO_OK;
@@ -598,7 +625,10 @@ int launch_reduce(const ReduceLaunch& a, zero_dtype_t gt, int64_t nblocks, void*
 }
 
 int launch_norm(const NormLaunch& a, void* stream) {
-  hipLaunchKernelGGL(norm_kernel, dim3(1), dim3(kNormThreads), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(norm_partial_kernel, dim3(kNormGroups), dim3(kNormThreads), 0, (hipStream_t)stream, a);
+  int rc = check_launch("norm");
+  if (rc) return rc;
+  hipLaunchKernelGGL(norm_final_kernel, dim3(1), dim3(kNormThreads), 0, (hipStream_t)stream, a);
   return check_launch("norm");
 }
 

@@ -32,10 +32,12 @@ constexpr int kThreads = 256;   // threads per workgroup (4 wave64s)
 constexpr int kVec = 8;         // elements per thread per tile
 constexpr int kTile = kThreads * kVec;
 constexpr int kMaxSeg = 24;     // gather pieces one launch of the update kernel can address
-constexpr int kNormThreads = 1024;    // the one-workgroup norm finalize
+constexpr int kNormThreads = 256;     // threads of the norm finalize workgroups
+constexpr int kNormGroups = 256;      // first-level workgroups of the norm finalize
 constexpr int kStateTileShift = 11;   // tiled state: 2048 elements of master, m, v per tile
 constexpr int64_t kStateTile = int64_t(1) << kStateTileShift;
 constexpr int kStreamBlocksPerCU = 3; // resident workgroups per CU of the streaming kernels
+constexpr int kStashBlocksPerCU = 4;  // ... of the update kernel that reads the fp32 stash
 
 // A rank piece as seen by one launch: local elements [.., end) map to gather
 // element (local index + delta).
@@ -97,7 +99,10 @@ struct ReduceLaunch {
 struct NormLaunch {
   const uint32_t* ws_flags;
   const double* ws_sums;
+  double* l2_sums;         // [kNormGroups]
+  uint32_t* l2_flags;      // [kNormGroups]
   int64_t nblocks;
+  int64_t chunk;           // partials per first-level workgroup
   double other_sumsq;
   double max_norm;
   uint32_t* overflow_out;
@@ -108,9 +113,12 @@ struct NormLaunch {
 // gradient-preparation grid: one 8-element vector per thread, one workgroup per
 // kTile elements; the workspace holds one fp64 partial and one overflow word per
 // workgroup
+// workgroup, then kNormGroups first-level sums and overflow words of the finalize
 inline int64_t reduce_blocks(int64_t S) { return (S + kTile - 1) / kTile; }
-inline size_t ws_sums_offset() { return 0; }
-inline size_t ws_flags_offset(int64_t S) { return (size_t)reduce_blocks(S) * sizeof(double); }
+inline size_t ws_l2_sums_offset() { return 0; }
+inline size_t ws_l2_flags_offset() { return (size_t)kNormGroups * sizeof(double); }
+inline size_t ws_sums_offset() { return ws_l2_flags_offset() + (size_t)kNormGroups * sizeof(uint32_t); }
+inline size_t ws_flags_offset(int64_t S) { return ws_sums_offset() + (size_t)reduce_blocks(S) * sizeof(double); }
 inline size_t ws_bytes(int64_t S) {
   return (ws_flags_offset(S) + (size_t)reduce_blocks(S) * sizeof(uint32_t) + 255) / 256 * 256;
 }
