@@ -136,12 +136,17 @@ def _flat(psi, world, rank, g, p, seed=3, **kw):
                       lr=1e-3, weight_decay=0.05, steps=2, seed=seed, **kw)
 
 
+# shard sizes on either side of the one-workgroup path's limit (8192 elements)
+SIZES = pytest.mark.parametrize("S", [5003, 20011], ids=["small", "large"])
+
+
+@SIZES
 @pytest.mark.parametrize("g", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("p", ["f32", "bf16", "f16"])
-def test_dtype_matrix(g, p):
-    run_workload(_flat(4 * 5003, 4, 3, g, p))
+def test_dtype_matrix(g, p, S):
+    run_workload(_flat(4 * S, 4, 3, g, p))
     if g == p:
-        run_workload(_flat(4 * 5003, 4, 3, g, p), layout=TILED)
+        run_workload(_flat(4 * S, 4, 3, g, p), layout=TILED)
 
 
 @pytest.mark.parametrize("world,rank,psi", [
@@ -164,9 +169,10 @@ def test_loss_scaled_fp16():
     run_workload(_flat(64 * 3001, 64, 63, "f16", "f16", loss_scale=65536.0, grad_zero_frac=0.01))
 
 
-def test_minimal_slice_stride():
-    """Slices packed with the smallest 16-byte-aligned stride (S = 4093, ld = 4096)."""
-    run_workload(_flat(4 * 4093, 4, 1, "bf16", "bf16"), ld_align=8)
+@pytest.mark.parametrize("S", [4093, 16381])
+def test_minimal_slice_stride(S):
+    """Slices packed with the smallest 16-byte-aligned stride (ld = S rounded up to 8)."""
+    run_workload(_flat(4 * S, 4, 1, "bf16", "bf16"), ld_align=8)
 
 
 def test_many_buckets_several_launches():
@@ -182,12 +188,13 @@ def test_many_buckets_several_launches():
         run_workload(dataclasses.replace(w, max_norm=1e-3, name="many_buckets_clip"), layout=layout)
 
 
+@SIZES
 @LAYOUTS
 @pytest.mark.parametrize("bad", ["+inf", "-inf", "nan", "f16_overflow"])
 @pytest.mark.parametrize("mode", ["fused", "stash"])
-def test_overflow_skips_bitwise(bad, mode, layout):
+def test_overflow_skips_bitwise(bad, mode, layout, S):
     gk = "f16" if bad == "f16_overflow" else "bf16"
-    w = _flat(8 * 3001, 8, 5, gk, gk, max_norm=(1.0 if mode == "stash" else 0.0))
+    w = _flat(8 * S, 8, 5, gk, gk, max_norm=(1.0 if mode == "stash" else 0.0))
     rig = Rig(w, layout=layout)
     say(f"overflow {bad} {mode}")
     sl_cpu, _ = rig.slices(1)
@@ -209,10 +216,11 @@ def test_overflow_skips_bitwise(bad, mode, layout):
     assert np.array_equal(rig.gather_np(), rig.gather0)
 
 
+@SIZES
 @LAYOUTS
 @pytest.mark.parametrize("mode", ["fused", "stash"])
-def test_forced_skip(mode, layout):
-    w = _flat(4 * 2000, 4, 2, "bf16", "bf16", max_norm=(1.0 if mode == "stash" else 0.0))
+def test_forced_skip(mode, layout, S):
+    w = _flat(4 * S, 4, 2, "bf16", "bf16", max_norm=(1.0 if mode == "stash" else 0.0))
     rig = Rig(w, layout=layout)
     _, sl_dev = rig.slices(1)
     skip = torch.ones(1, dtype=torch.int32, device="cuda")
@@ -232,10 +240,11 @@ def test_forced_skip(mode, layout):
     assert np.array_equal(rig.gather_np(), rig.gather0)
 
 
+@SIZES
 @LAYOUTS
-def test_no_flag_in_place_matches(layout):
+def test_no_flag_in_place_matches(layout, S):
     """Fused step without an overflow flag, updated in place."""
-    w = _flat(4 * 3000 + 3, 4, 3, "bf16", "bf16")
+    w = _flat(4 * S + 3, 4, 3, "bf16", "bf16")
     rig = Rig(w, layout=layout)
     sl_cpu, sl_dev = rig.slices(1)
     rig.fused(sl_dev, rig.A, rig.A, 1, overflow=False)

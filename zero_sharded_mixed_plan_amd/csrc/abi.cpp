@@ -281,6 +281,22 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
   }
 
   int rc = ZERO_OK;
+  if (!stash && S <= zk::kSmallShard && groups.size() == 1) {
+    // one workgroup decides the skip before writing: a single launch
+    L.v_lo = 0;
+    L.v_hi = nvec;
+    L.nseg = groups[0].count;
+    for (int s = 0; s < L.nseg; ++s) {
+      const auto& B = plan->buckets[groups[0].first + s];
+      L.seg[s].end = B.local_off + B.shard;
+      L.seg[s].delta = (B.base + (int64_t)A.rank * B.shard) - B.local_off;
+    }
+    rc = zk::record_event(A.ev_begin, stream);
+    if (rc) return rc;
+    rc = zk::launch_small_step(L, A.grad_dtype, A.param_dtype, stream);
+    if (rc) return rc;
+    return zk::record_event(A.ev_end, stream);
+  }
   if (strict) rc = zk::launch_fill_u32(A.overflow_out, 0u, stream);
   if (rc) return rc;
   rc = zk::record_event(A.ev_begin, stream);

@@ -355,6 +355,75 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
   if (!STASH && a.overflow != nullptr && bad) atomicOr(a.overflow, 1u);
 }
 
+// Small shards (S <= kSmallShard) in one launch: one workgroup, one 8-element
+// vector per thread.  Every thread reduces its slices first and keeps g in
+// registers; a workgroup-wide OR of the overflow decides the skip before any
+// output is written, so a skipped step writes nothing and needs no restore pass
+// or flag reset (the two extra launches of the multi-workgroup path, which
+// dominate a step this small).
+// (batches of 8 slices whatever N: 1024 threads leave 128 registers each)
+template <class GT, class PT>
+__global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLaunch a) {
+  if (a.skip_in != nullptr && *a.skip_in != 0u) {
+    if (a.overflow != nullptr && threadIdx.x == 0) *a.overflow = 1u;
+    return;
+  }
+  const int64_t j0 = (int64_t)threadIdx.x * kVec;
+  const int64_t rest = a.S - j0;
+  const int cnt = rest >= kVec ? kVec : (rest > 0 ? (int)rest : 0);
+  float g[8];
+  bool bad = false;
+  if (cnt == kVec) {
+    float acc[8];
+    reduce8<GT, Batch<GT, false>::value>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes,
+                                         a.n, acc);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, a.inv_scale);
+  } else {
+    for (int e = 0; e < 8; ++e) {
+      g[e] = 0.0f;
+      if (e < cnt) {
+        const float acc = reduce1<GT>(static_cast<const char*>(a.grad) + (j0 + e) * GT::bytes, a.ld_bytes, a.n);
+        g[e] = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, a.inv_scale);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bad |= !__builtin_isfinite(g[e]);
+  const int any_bad = __syncthreads_or(bad ? 1 : 0);
+  if (a.overflow != nullptr && threadIdx.x == 0) *a.overflow = any_bad ? 1u : 0u;
+  if (any_bad || cnt == 0) return;
+  float p[8], m[8], v[8];
+  if (cnt == kVec) {
+    const int64_t o0 = state_off(a, j0);
+    ld8(a.p_in + o0, p);
+    ld8(a.m_in + o0, m);
+    ld8(a.v_in + o0, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) adamw1(p[e], m[e], v[e], g[e], a.c);
+    st8(a.p_out + o0, p);
+    st8(a.m_out + o0, m);
+    st8(a.v_out + o0, v);
+    const int64_t d0 = delta_of(a, j0);
+    if (delta_of(a, j0 + kVec - 1) == d0) {
+      store_params8<PT>(a.gather + (j0 + d0) * PT::bytes, p);
+    } else {
+      for (int e = 0; e < 8; ++e) store_param1<PT>(a.gather + (j0 + e + delta_of(a, j0 + e)) * PT::bytes, p[e]);
+    }
+  } else {
+    for (int e = 0; e < cnt; ++e) {
+      const int64_t j = j0 + e;
+      const int64_t oj = state_off(a, j);
+      float pe = a.p_in[oj], me = a.m_in[oj], ve = a.v_in[oj];
+      adamw1(pe, me, ve, g[e], a.c);
+      a.p_out[oj] = pe;
+      a.m_out[oj] = me;
+      a.v_out[oj] = ve;
+      store_param1<PT>(a.gather + (j + delta_of(a, j)) * PT::bytes, pe);
+    }
+  }
+}
+
 // On a skipped fused step: rewrite the rank's gather pieces from master_in, so
 // they keep the pre-step parameters.  A no-op unless *cond != 0.
 template <class PT>
@@ -584,6 +653,30 @@ int launch_step(const StepLaunch& a, zero_dtype_t gt, zero_dtype_t pt, bool stas
   }
   if (rc != ZERO_OK) return rc;
   return check_launch("step");
+}
+
+template <class GT>
+static int small_pt(const StepLaunch& a, zero_dtype_t pt, hipStream_t st) {
+  const dim3 g(1), b(kSmallThreads);
+  switch (pt) {
+    case ZERO_F32: hipLaunchKernelGGL((small_step_kernel<GT, TF32>), g, b, 0, st, a); return ZERO_OK;
+    case ZERO_BF16: hipLaunchKernelGGL((small_step_kernel<GT, TBF16>), g, b, 0, st, a); return ZERO_OK;
+    case ZERO_F16: hipLaunchKernelGGL((small_step_kernel<GT, TF16>), g, b, 0, st, a); return ZERO_OK;
+  }
+  return fail(ZERO_EINVAL, "unsupported parameter dtype");
+}
+
+int launch_small_step(const StepLaunch& a, zero_dtype_t gt, zero_dtype_t pt, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  int rc;
+  switch (gt) {
+    case ZERO_F32: rc = small_pt<TF32>(a, pt, st); break;
+    case ZERO_BF16: rc = small_pt<TBF16>(a, pt, st); break;
+    case ZERO_F16: rc = small_pt<TF16>(a, pt, st); break;
+    default: return fail(ZERO_EINVAL, "unsupported gradient dtype");
+  }
+  if (rc != ZERO_OK) return rc;
+  return check_launch("small step");
 }
 
 int launch_recast(const StepLaunch& a, zero_dtype_t pt, const u32* cond, void* stream) {

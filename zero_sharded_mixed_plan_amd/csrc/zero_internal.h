@@ -38,6 +38,8 @@ constexpr int kStateTileShift = 11;   // tiled state: 2048 elements of master, m
 constexpr int64_t kStateTile = int64_t(1) << kStateTileShift;
 constexpr int kStreamBlocksPerCU = 3; // resident workgroups per CU of the streaming kernels
 constexpr int kStashBlocksPerCU = 4;  // ... of the update kernel that reads the fp32 stash
+constexpr int kSmallThreads = 1024;   // one-workgroup path for small shards ...
+constexpr int64_t kSmallShard = (int64_t)kSmallThreads * kVec;  // ... of at most this many elements
 
 // A rank piece as seen by one launch: local elements [.., end) map to gather
 // element (local index + delta).
@@ -127,6 +129,7 @@ inline size_t ws_bytes(int64_t S) {
 int launch_fill_u32(uint32_t* p, uint32_t value, void* stream);
 int launch_step(const StepLaunch& a, zero_dtype_t gt, zero_dtype_t pt, bool stash, void* stream);
 int launch_recast(const StepLaunch& a, zero_dtype_t pt, const uint32_t* cond, void* stream);
+int launch_small_step(const StepLaunch& a, zero_dtype_t gt, zero_dtype_t pt, void* stream);
 int launch_reduce(const ReduceLaunch& a, zero_dtype_t gt, int64_t nblocks, void* stream);
 int launch_norm(const NormLaunch& a, void* stream);
 int record_event(void* ev, void* stream);
