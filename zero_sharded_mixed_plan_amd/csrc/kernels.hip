@@ -606,21 +606,27 @@ static void go_step(const StepLaunch& a, unsigned blocks, size_t lds, hipStream_
 // Resident workgroups per CU of the streaming kernels.  Fewer concurrent waves
 // keep fewer DRAM pages open per stream: on the GPT-2 1.5B and Llama-7B shards
 // 3 workgroups (12 wave64s) per CU stream 5% faster than the 4-5 the registers
-// allow, and 1 per CU is too few.  The cap is imposed by reserving LDS the
-// kernels do not otherwise use.
+// allow, and 1 per CU is too few.  The cap is imposed by reserving dynamic LDS
+// the kernels do not otherwise use.  A workgroup's dynamic plus static LDS must
+// stay within the per-workgroup limit, or the dispatch is invalid: the
+// reservation leaves kStaticLdsRoom bytes for the kernels' own small arrays.
 static size_t occupancy_lds(int per_cu) {
   static thread_local int dev_cached = -1;
-  static thread_local size_t lds_cu = 0;
+  static thread_local size_t lds_cu = 0, lds_block = 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev != dev_cached) {
-    int v = 0;
+    int v = 0, b = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess) v = 0;
+    if (hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) b = 0;
     lds_cu = (size_t)v;
+    lds_block = (size_t)b;
     dev_cached = dev;
   }
-  if (lds_cu == 0) return 0;
-  return (lds_cu / (size_t)per_cu) / 512 * 512;
+  size_t share = lds_cu / (size_t)per_cu;
+  if (share > lds_block) share = lds_block;
+  if (share <= kStaticLdsRoom) return 0;
+  return (share - kStaticLdsRoom) / 512 * 512;
 }
 
 template <class GT, bool STASH>
