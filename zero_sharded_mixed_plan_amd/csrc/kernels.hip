@@ -604,17 +604,22 @@ static void go_step(const StepLaunch& a, unsigned blocks, size_t lds, hipStream_
 }
 
 // Resident workgroups per CU of the streaming kernels.  Fewer concurrent waves
-// keep fewer DRAM pages open per stream: on the GPT-2 1.5B and Llama-7B shards
-// 3 workgroups (12 wave64s) per CU stream 5% faster than the 4-5 the registers
-// allow, and 1 per CU is too few.  The cap is imposed by reserving dynamic LDS
-// the kernels do not otherwise use.  A workgroup's dynamic plus static LDS must
-// stay within the per-workgroup limit, or the dispatch is invalid: the
-// reservation leaves kStaticLdsRoom bytes for the kernels' own small arrays.
+// keep fewer DRAM pages open per stream.  Measured on the GPT-2 1.5B and
+// Llama-7B shards, 2 workgroups (8 wave64s) per CU stream the fused update and
+// the reduction 7-8% faster than 3 or 4, while 1 per CU is too few to cover
+// the latency; the stash-mode update, with four streams, is best at 3-4.
+// The cap is imposed by reserving dynamic LDS the kernels do not otherwise use.
+// The reservation sits halfway between the sizes at which per_cu + 1 and
+// per_cu workgroups just fit, in 2 KiB steps, so that neither the allocation
+// granularity nor a kernel's own small __shared__ arrays move the count: a
+// reservation of exactly a third of the CU's LDS already admits only two.  A
+// workgroup's dynamic plus static LDS must also stay within the per-workgroup
+// limit, or the dispatch is invalid; kStaticLdsRoom is kept free for that.
 static size_t occupancy_lds(int per_cu) {
   static thread_local int dev_cached = -1;
   static thread_local size_t lds_cu = 0, lds_block = 0;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (per_cu <= 0 || hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev != dev_cached) {
     int v = 0, b = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess) v = 0;
@@ -623,10 +628,13 @@ static size_t occupancy_lds(int per_cu) {
     lds_block = (size_t)b;
     dev_cached = dev;
   }
-  size_t share = lds_cu / (size_t)per_cu;
-  if (share > lds_block) share = lds_block;
-  if (share <= kStaticLdsRoom) return 0;
-  return (share - kStaticLdsRoom) / 512 * 512;
+  const size_t fits = lds_cu / (size_t)per_cu;               // per_cu workgroups fit at or below
+  const size_t excludes = lds_cu / (size_t)(per_cu + 1);     // per_cu + 1 cannot fit above
+  if (fits <= kStaticLdsRoom) return 0;
+  size_t r = ((fits - kStaticLdsRoom + excludes) / 2) / 2048 * 2048;
+  if (lds_block > kStaticLdsRoom && r > lds_block - kStaticLdsRoom) r = lds_block - kStaticLdsRoom;
+  if (lds_block <= kStaticLdsRoom || r <= excludes) return 0;  // no reservation that enforces the cap
+  return r;
 }
 
 template <class GT, bool STASH>

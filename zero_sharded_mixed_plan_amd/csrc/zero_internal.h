@@ -36,7 +36,7 @@ constexpr int kNormThreads = 256;     // threads of the norm finalize workgroups
 constexpr int kNormGroups = 256;      // first-level workgroups of the norm finalize
 constexpr int kStateTileShift = 11;   // tiled state: 2048 elements of master, m, v per tile
 constexpr int64_t kStateTile = int64_t(1) << kStateTileShift;
-constexpr int kStreamBlocksPerCU = 3; // resident workgroups per CU of the streaming kernels
+constexpr int kStreamBlocksPerCU = 2; // resident workgroups per CU of the streaming kernels
 constexpr int kStashBlocksPerCU = 4;  // ... of the update kernel that reads the fp32 stash
 constexpr size_t kStaticLdsRoom = 1024;  // LDS left for a streaming kernel's own __shared__ arrays
 constexpr int kSmallThreads = 1024;   // one-workgroup path for small shards ...
