@@ -165,6 +165,19 @@ def test_world_and_alignment(world, rank, psi):
     run_workload(_flat(psi, world, rank, "bf16", "bf16"), layout=TILED)
 
 
+# Every compiled form of the slice reduction: 4 and 8 slices in narrow batches
+# (fp32: one or two batches of 4), 16 / 32 / 64 in wide batches (fp32: 8 per
+# batch), and 24, which no batch size divides (the runtime-N form), each in
+# the fused update and in the clipped path's reduction.
+@pytest.mark.parametrize("world", [4, 8, 16, 24, 32, 64])
+@pytest.mark.parametrize("g", ["f32", "bf16", "f16"])
+def test_batch_forms(world, g):
+    psi = world * 4099
+    p = "bf16" if g != "f32" else "f32"
+    run_workload(_flat(psi, world, world - 1, g, p), layout=TILED)
+    run_workload(_flat(psi, world, world // 2, g, p, max_norm=0.05), layout=TILED)
+
+
 def test_loss_scaled_fp16():
     run_workload(_flat(64 * 3001, 64, 63, "f16", "f16", loss_scale=65536.0, grad_zero_frac=0.01))
 

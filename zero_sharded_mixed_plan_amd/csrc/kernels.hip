@@ -252,6 +252,58 @@ __device__ __forceinline__ void reduce8(const char* base, int64_t ld_bytes, int 
   }
 }
 
+// The same sum when N is a whole number of batches, NBATCH = N / NB known at
+// compile time.  The loop unrolls into straight-line code with two register
+// buffers taking turns, so every load is unconditional, nothing is copied
+// between buffers, and each add waits only for its own slice: while batch i is
+// added, the loads of batch i + 1 are in flight.  (In the runtime-N form the
+// compiler waits for every outstanding load before the first add of a batch.)
+// ubase is uniform across the workgroup and toff is the lane's byte offset.
+template <class T, int NB>
+__device__ __forceinline__ void load_batch(Raw<T> (&r)[NB], const char* ubase, int64_t ld_bytes,
+                                           uint32_t toff) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b) r[b] = ld_raw<T>(ubase + (int64_t)b * ld_bytes + toff);
+}
+
+template <class T, int NB>
+__device__ __forceinline__ void add_batch(const Raw<T> (&r)[NB], bool first, float acc[8]) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float w[8];
+    widen8<T>(r[b], w);
+    if (first && b == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = w[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + w[e];
+    }
+  }
+}
+
+// after_last_issue() runs once, right after the loads of the last batch are
+// issued (the caller's state loads go there).
+template <class T, int NB, int NBATCH, class F>
+__device__ __forceinline__ void reduce8_fixed(const char* ubase, int64_t ld_bytes, uint32_t toff,
+                                              float acc[8], F&& after_last_issue) {
+  static_assert(NBATCH >= 1, "at least one batch");
+  Raw<T> r[2][NB];
+  load_batch<T, NB>(r[0], ubase, ld_bytes, toff);
+  if (NBATCH == 1) after_last_issue();
+#pragma unroll
+  for (int i = 0; i < NBATCH; ++i) {
+    if (i + 1 < NBATCH) {
+      load_batch<T, NB>(r[(i + 1) & 1], ubase + (int64_t)(i + 1) * NB * ld_bytes, ld_bytes, toff);
+      if (i + 2 == NBATCH) after_last_issue();
+    }
+    add_batch<T, NB>(r[i & 1], i == 0, acc);
+    // keep later batches' loads below this batch's adds: at most two batches
+    // (and the state) are in flight, which bounds the registers held
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 template <class T>
 __device__ __forceinline__ float reduce1(const char* base, int64_t ld_bytes, int n) {
   float acc = ld_one<T>(base);
@@ -284,7 +336,7 @@ __device__ __forceinline__ int64_t delta_of(const StepLaunch& a, int64_t j) {
 // the update kernel (fused: N slices in; stash: fp32 g in)
 // ---------------------------------------------------------------------------
 
-template <class GT, class PT, bool STASH, bool WIDE>
+template <class GT, class PT, bool STASH, bool WIDE, int NBATCH>
 __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
   if (a.skip_in != nullptr && *a.skip_in != 0u) {
     // skipped by the caller: report it like an overflow so the fused step's
@@ -302,17 +354,30 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
   bool bad = false;
   if (j0 + kVec <= a.S) {
     const int64_t o0 = state_off(a, j0);
-    ld8(a.p_in + o0, p);
-    ld8(a.m_in + o0, m);
-    ld8(a.v_in + o0, s);
+    auto load_state = [&]() {
+      ld8(a.p_in + o0, p);
+      ld8(a.m_in + o0, m);
+      ld8(a.v_in + o0, s);
+    };
     if (STASH) {
+      load_state();
       ld8(a.g_stash + j0, g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) g[e] = g[e] * clip;
     } else {
+      constexpr int NB = Batch<GT, WIDE>::value;
       float acc[8];
-      reduce8<GT, Batch<GT, WIDE>::value>(static_cast<const char*>(a.grad) + j0 * GT::bytes,
-                                          a.ld_bytes, a.n, acc);
+      if constexpr (NBATCH > 0) {
+        // the state loads go out with the last batch of slices, so they hold
+        // no registers while the earlier batches stream in
+        const char* ubase = static_cast<const char*>(a.grad) +
+                            (a.v_lo + (int64_t)blockIdx.x * kThreads) * (kVec * GT::bytes);
+        reduce8_fixed<GT, NB, NBATCH>(ubase, a.ld_bytes, threadIdx.x * (uint32_t)(kVec * GT::bytes), acc,
+                                      load_state);
+      } else {
+        load_state();
+        reduce8<GT, NB>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes, a.n, acc);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, a.inv_scale);
@@ -458,7 +523,7 @@ __device__ __forceinline__ double wave_sum(double x) {
   return x;
 }
 
-template <class GT, bool WIDE>
+template <class GT, bool WIDE, int NBATCH>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) {
   // one 8-element vector per thread; workgroup b owns vectors [256 b, 256 b + 256),
   // so the partition (and every partial sum) depends only on S
@@ -469,8 +534,14 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) 
     const int64_t j0 = v * kVec;
     if (j0 + kVec <= a.S) {
       float acc[8], g[8];
-      reduce8<GT, Batch<GT, WIDE>::value>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes,
-                                          a.n, acc);
+      constexpr int NB = Batch<GT, WIDE>::value;
+      if constexpr (NBATCH > 0) {
+        const char* ubase = static_cast<const char*>(a.grad) + (int64_t)blockIdx.x * (kTile * GT::bytes);
+        reduce8_fixed<GT, NB, NBATCH>(ubase, a.ld_bytes, threadIdx.x * (uint32_t)(kVec * GT::bytes), acc,
+                                      [] {});
+      } else {
+        reduce8<GT, NB>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes, a.n, acc);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, a.inv_scale);
@@ -595,12 +666,29 @@ int launch_fill_u32(u32* p, u32 value, void* stream) {
   return check_launch("fill");
 }
 
+// Batches of N / NB known at compile time for the world sizes that are a
+// whole number (1, 2 or 4) of batches -- 4 and 8 in narrow batches, 16, 32 and
+// 64 (fp32: 16 and 32) in wide ones; the runtime-N form for every other N.
+template <class GT, class PT, bool STASH, bool WIDE>
+static void go_step_full(const StepLaunch& a, unsigned blocks, size_t lds, hipStream_t st) {
+  constexpr int NB = Batch<GT, WIDE>::value;
+  const int nbatch = (!STASH && a.n % NB == 0) ? a.n / NB : 0;
+  const dim3 g(blocks), b(kThreads);
+  switch (nbatch) {
+    case 1: hipLaunchKernelGGL((step_kernel<GT, PT, STASH, WIDE, 1>), g, b, lds, st, a); return;
+    case 2: hipLaunchKernelGGL((step_kernel<GT, PT, STASH, WIDE, 2>), g, b, lds, st, a); return;
+    case 4: hipLaunchKernelGGL((step_kernel<GT, PT, STASH, WIDE, 4>), g, b, lds, st, a); return;
+    default: hipLaunchKernelGGL((step_kernel<GT, PT, STASH, WIDE, 0>), g, b, lds, st, a); return;
+  }
+}
+
+// wide batches when N > 8; the turn-taking reduction when the batch divides N
 template <class GT, class PT, bool STASH>
 static void go_step(const StepLaunch& a, unsigned blocks, size_t lds, hipStream_t st) {
   if (!STASH && a.n > 8)
-    hipLaunchKernelGGL((step_kernel<GT, PT, STASH, true>), dim3(blocks), dim3(kThreads), lds, st, a);
+    go_step_full<GT, PT, STASH, true>(a, blocks, lds, st);
   else
-    hipLaunchKernelGGL((step_kernel<GT, PT, STASH, false>), dim3(blocks), dim3(kThreads), lds, st, a);
+    go_step_full<GT, PT, STASH, false>(a, blocks, lds, st);
 }
 
 // Resident workgroups per CU of the streaming kernels.  Fewer concurrent waves
@@ -708,24 +796,33 @@ int launch_recast(const StepLaunch& a, zero_dtype_t pt, const u32* cond, void* s
   return check_launch("recast");
 }
 
+template <class GT, bool WIDE>
+static void go_reduce(const ReduceLaunch& a, dim3 grid, size_t lds, hipStream_t st) {
+  constexpr int NB = Batch<GT, WIDE>::value;
+  const int nbatch = a.n % NB == 0 ? a.n / NB : 0;
+  const dim3 blk(kThreads);
+  switch (nbatch) {
+    case 1: hipLaunchKernelGGL((reduce_kernel<GT, WIDE, 1>), grid, blk, lds, st, a); return;
+    case 2: hipLaunchKernelGGL((reduce_kernel<GT, WIDE, 2>), grid, blk, lds, st, a); return;
+    case 4: hipLaunchKernelGGL((reduce_kernel<GT, WIDE, 4>), grid, blk, lds, st, a); return;
+    default: hipLaunchKernelGGL((reduce_kernel<GT, WIDE, 0>), grid, blk, lds, st, a); return;
+  }
+}
+
+template <class GT>
+static void go_reduce_wide(const ReduceLaunch& a, dim3 grid, size_t lds, hipStream_t st) {
+  if (a.n > 8) go_reduce<GT, true>(a, grid, lds, st);
+  else go_reduce<GT, false>(a, grid, lds, st);
+}
+
 int launch_reduce(const ReduceLaunch& a, zero_dtype_t gt, int64_t nblocks, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  const bool wide = a.n > 8;
   const size_t lds = occupancy_lds(kStreamBlocksPerCU);
-  const dim3 grid((unsigned)nblocks), blk(kThreads);
+  const dim3 grid((unsigned)nblocks);
   switch (gt) {
-    case ZERO_F32:
-      if (wide) hipLaunchKernelGGL((reduce_kernel<TF32, true>), grid, blk, lds, st, a);
-      else hipLaunchKernelGGL((reduce_kernel<TF32, false>), grid, blk, lds, st, a);
-      break;
-    case ZERO_BF16:
-      if (wide) hipLaunchKernelGGL((reduce_kernel<TBF16, true>), grid, blk, lds, st, a);
-      else hipLaunchKernelGGL((reduce_kernel<TBF16, false>), grid, blk, lds, st, a);
-      break;
-    case ZERO_F16:
-      if (wide) hipLaunchKernelGGL((reduce_kernel<TF16, true>), grid, blk, lds, st, a);
-      else hipLaunchKernelGGL((reduce_kernel<TF16, false>), grid, blk, lds, st, a);
-      break;
+    case ZERO_F32: go_reduce_wide<TF32>(a, grid, lds, st); break;
+    case ZERO_BF16: go_reduce_wide<TBF16>(a, grid, lds, st); break;
+    case ZERO_F16: go_reduce_wide<TF16>(a, grid, lds, st); break;
     default: return fail(ZERO_EINVAL, "unsupported gradient dtype");
   }
   return check_launch("reduce");
