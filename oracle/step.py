@@ -193,3 +193,18 @@ def write_gather(gather: np.ndarray, segments, params: np.ndarray) -> None:
     """
     for goff, loff, seg_len, _valid in segments:
         gather[goff:goff + seg_len] = params[loff:loff + seg_len]
+
+
+def read_pieces(full: np.ndarray, segments) -> np.ndarray:
+    """The rank's [S] local gradient read out of a full flat gradient (ZeRO-1:
+    gradients all-reduced in full, each rank updating only the range it owns;
+    handbook chapter, section "三个级别"; "PaddlePaddle ZeRO优化…", section
+    "第一层：只分片优化器状态（ZeRO-1）").  The rank's pieces sit where its
+    parameter slots sit in the gather buffer, so this is write_gather read
+    backwards.  segments: (gather_off, local_off, seg_len, valid) per bucket.
+    """
+    S = sum(seg_len for _g, _l, seg_len, _v in segments)
+    out = np.empty(S, dtype=full.dtype)
+    for goff, loff, seg_len, _valid in segments:
+        out[loff:loff + seg_len] = full[goff:goff + seg_len]
+    return out
