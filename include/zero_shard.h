@@ -150,24 +150,48 @@ int64_t zero_state_numel(const zero_plan_t* plan, int32_t layout);
 size_t zero_workspace_bytes(const zero_plan_t* plan);
 
 /*
+ * Where the gradient buffers a step reads come from.
+ *
+ * ZERO_GRAD_SHARD: each buffer is this rank's [S] shard, local index j.  With
+ * N buffers they are the N ranks' contributions that the reduce-scatter sums
+ * (the fused ZeRO-2 step; handbook chapter "ZeRO 与 FSDP：切分优化器状态、
+ * 梯度与参数", section "从零实现 ZeRO 的 Adam", reduce_scatter with SUM); with
+ * one buffer it is the stored reduce-scatter output, still the SUM over ranks
+ * (ZeRO-2 with the collective run separately: a gradient partition of 2*Psi/N
+ * bytes; "论文专题讲解：ZeRO…", section "ZeRO-DP 三阶段").
+ * ZERO_GRAD_FULL: each buffer is a whole flat gradient of
+ * zero_plan_padded_numel elements in the gather buffer's layout, and the rank
+ * reads its pieces at the offsets of its gather slots.  With one buffer this
+ * is ZeRO-1 (P_os): gradients all-reduced (SUM) in full on every rank, each
+ * rank updating only its partition (the handbook chapter, section "三个级别";
+ * "PaddlePaddle ZeRO优化…", section "第一层：只分片优化器状态（ZeRO-1）").
+ */
+typedef enum zero_grad_layout {
+  ZERO_GRAD_SHARD = 0,
+  ZERO_GRAD_FULL = 1
+} zero_grad_layout_t;
+
+/*
  * Gradient preparation, first pass of the clipped step (global-norm clipping
  * needs the norm of the whole gradient before any element is updated).
  *
- * For every local element j < S:
- *   acc = slice_0[j] + slice_1[j] + ... + slice_{N-1}[j]   (fp32, ascending k)
+ * For every local element j < S, with C = grad_count (0 means N):
+ *   acc = slice_0[j] + slice_1[j] + ... + slice_{C-1}[j]   (fp32, ascending k)
  *   g   = (acc / N) * inv_scale                              (zero_adam.py g /= world;
  *                                                             GradScaler unscale)
- * Slice k starts at grad + k * grad_ld elements (dtype grad_dtype), ld >= S,
- * 16-byte aligned start and stride.  If g_out != NULL, g is stored there (fp32,
- * [S], 16-byte aligned).  Per workgroup, an overflow word (any non-finite g)
- * and, if want_sumsq, the float64 sum of g^2 go to `ws`
- * (zero_workspace_bytes).  The partition of elements over workgroups depends
- * only on S, so the sums are deterministic run to run.
- * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EHIP.
+ * Slice k (ZERO_GRAD_SHARD layout, [S]) starts at grad + k * grad_ld elements
+ * (dtype grad_dtype), 16-byte aligned start; with C > 1, ld >= S and ld a
+ * 16-byte multiple (ignored when C == 1).  C == 1 reads a stored
+ * reduce-scatter output (already summed over the ranks).  If g_out != NULL, g
+ * is stored there (fp32, [S], 16-byte aligned).  Per workgroup, an overflow
+ * word (any non-finite g) and, if want_sumsq, the float64 sum of g^2 go to
+ * `ws` (zero_workspace_bytes).  The partition of elements over workgroups
+ * depends only on S, so the sums are deterministic run to run.
+ * Errors: ZERO_EINVAL (incl. C < 0), ZERO_EALIGN, ZERO_EHIP.
  */
 int zero_reduce_shard(const zero_plan_t* plan, const void* grad, int64_t grad_ld,
-                      zero_dtype_t grad_dtype, float inv_scale, float* g_out, void* ws,
-                      int32_t want_sumsq, void* stream);
+                      int32_t grad_count, zero_dtype_t grad_dtype, float inv_scale, float* g_out,
+                      void* ws, int32_t want_sumsq, void* stream);
 
 /*
  * Second pass: finalize what zero_reduce_shard left in `ws` (two small launches:
@@ -188,10 +212,12 @@ int zero_shard_norm(const zero_plan_t* plan, void* ws, double other_ranks_sumsq,
 /* Arguments of zero_adam_step (host struct; pointers are device addresses). */
 typedef struct zero_adam_args {
   int32_t rank;              /* 0 <= rank < N                                      */
-  /* gradient source: either N slices (fused step) ...                          */
-  const void* grad;          /* slice k at grad + k*grad_ld elements               */
-  int64_t grad_ld;           /* elements, >= S                                     */
+  /* gradient source: either C gradient buffers summed in the step (fused) ... */
+  const void* grad;          /* buffer k at grad + k*grad_ld elements              */
+  int64_t grad_ld;           /* elements between buffers (unused when C == 1)     */
   zero_dtype_t grad_dtype;
+  int32_t grad_count;        /* C: 0 = N (one per rank); 1 = an already summed one */
+  int32_t grad_layout;       /* zero_grad_layout_t                                 */
   float inv_scale;           /* fp32(1 / loss scale); 1 without loss scaling       */
   /* ... or the fp32 gradient written by zero_reduce_shard (then grad is ignored) */
   const float* g_stash;
@@ -228,10 +254,17 @@ typedef struct zero_adam_args {
  * Per element (zero_adam.py step() with decoupled weight decay; constants
  * computed in float64 and rounded once to fp32: b1, b2, 1-b1, 1-b2,
  * bc1 = 1-b1^step, bc2 = 1-b2^step, lr, eps, dec = 1-lr*wd):
- *   g      = fused: (sum_k slice_k / N) * inv_scale   |  stash: g_stash * clip_coef
+ *   g      = fused: (sum_{k<C} buffer_k[piece(j)] / N) * inv_scale
+ *            stash: g_stash * clip_coef
  *   m'     = b1*m + (1-b1)*g;     v' = b2*v + (1-b2)*(g*g)
  *   m_hat  = m'/bc1;  v_hat = v'/bc2;  u = (lr*m_hat) / (sqrt(v_hat) + eps)
  *   master'= dec*master - u;  gather[slot(j)] = round_to_nearest_even(master')
+ *
+ * Gradient buffers (zero_grad_layout_t): ZERO_GRAD_SHARD, [S] each, 16-byte
+ * aligned, stride grad_ld >= S a 16-byte multiple when C > 1; ZERO_GRAD_FULL,
+ * [zero_plan_padded_numel] each, element aligned, stride grad_ld >= that size
+ * a 16-byte multiple when C > 1, read at the rank's gather offsets.  The sum
+ * is always divided by N, the plan's world size.
  *
  * Overflow handling (GradScaler skips the optimizer step on inf/NaN):
  *  - fused mode: the flag is computed in the same pass over the slices.  The

@@ -174,17 +174,22 @@ class Rig:
             return tuple(x.cpu().numpy() for x in unpack_state(bufs[0], self.S))
         return tuple(x.cpu().numpy() for x in bufs)
 
-    def fused(self, sl_dev, src, dst, t, overflow=True, skip=None):
-        a = Z.adam_args(grad=sl_dev.data_ptr(), grad_ld=self.ld, grad_dtype=CODE[self.w.grad_dtype],
+    def fused(self, sl_dev, src, dst, t, overflow=True, skip=None, count=0, layout=Z.ZERO_GRAD_SHARD,
+              ld=None):
+        """The fused step on gradient buffers sl_dev (rows at stride ld, default
+        the rig's slice stride): count buffers (0 = N) in the given layout."""
+        a = Z.adam_args(grad=sl_dev.data_ptr(), grad_ld=self.ld if ld is None else ld,
+                        grad_dtype=CODE[self.w.grad_dtype], grad_count=count, grad_layout=layout,
                         inv_scale=1.0 / self.w.loss_scale,
                         overflow_out=self.flag.data_ptr() if overflow else None,
                         skip_in=skip, **self.state_args(src, dst), **self.common(t))
         Z.zero_adam_step(self.plan, a, torch.cuda.current_stream().cuda_stream)
 
-    def reduce_norm(self, sl_dev, other=0.0, max_norm=None):
+    def reduce_norm(self, sl_dev, other=0.0, max_norm=None, count=0):
         st = torch.cuda.current_stream().cuda_stream
         Z.zero_reduce_shard(self.plan, sl_dev.data_ptr(), self.ld, CODE[self.w.grad_dtype],
-                            1.0 / self.w.loss_scale, self.g.data_ptr(), self.ws.data_ptr(), True, st)
+                            1.0 / self.w.loss_scale, self.g.data_ptr(), self.ws.data_ptr(), True, st,
+                            grad_count=count)
         Z.zero_shard_norm(self.plan, self.ws.data_ptr(), other,
                           self.w.max_norm if max_norm is None else max_norm, self.flag.data_ptr(),
                           self.sumsq.data_ptr(), self.clip.data_ptr(), st)

@@ -115,6 +115,13 @@ def _good(plan, **over):
     (dict(m_out=BASE + (4 << 32)), Z.ZERO_EINVAL),       # two outputs overlap
     (dict(gather=BASE + (4 << 32) + 64), Z.ZERO_EINVAL),  # gather overlaps master_out
     (dict(v_out=BASE + 16), Z.ZERO_EINVAL),              # output overlaps the slices
+    (dict(grad_count=-1), Z.ZERO_EINVAL),
+    (dict(grad_layout=2), Z.ZERO_EINVAL),                # unknown gradient layout
+    (dict(grad_layout=1, grad_count=1, grad=BASE + 1), Z.ZERO_EALIGN),  # element alignment
+    (dict(grad_count=2, grad_ld=4803), Z.ZERO_EALIGN),   # stride not a 16-byte multiple
+    (dict(grad_layout=1, grad_ld=19_000), Z.ZERO_EINVAL),  # 4 full buffers need ld >= 19,212
+    (dict(grad_layout=1, grad_count=1,                   # a full buffer reaching master_out
+          grad=BASE + (4 << 32) - 64), Z.ZERO_EINVAL),
 ])
 def test_step_validation(over, code):
     plan = Z.Plan(W.numels(W.toy_mlp()), 4)
@@ -145,6 +152,12 @@ def test_reduce_and_norm_validation():
         Z.zero_reduce_shard(plan, BASE, 16, Z.ZERO_BF16, 1.0, 0, BASE, True)
     assert e.value.code == Z.ZERO_EINVAL          # ld < S = 25
     with pytest.raises(Z.ZeroError) as e:
+        Z.zero_reduce_shard(plan, BASE, 32, Z.ZERO_BF16, 1.0, 0, BASE, True, grad_count=-2)
+    assert e.value.code == Z.ZERO_EINVAL
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_reduce_shard(plan, BASE, 20, Z.ZERO_BF16, 1.0, 0, BASE, True, grad_count=2)
+    assert e.value.code == Z.ZERO_EINVAL          # two buffers, ld < S
+    with pytest.raises(Z.ZeroError) as e:
         Z.zero_shard_norm(plan, BASE, -1.0, 1.0, 0, 0, 0)
     assert e.value.code == Z.ZERO_EINVAL
     with pytest.raises(Z.ZeroError) as e:
@@ -171,3 +184,28 @@ def test_tiled_state_validation(over, code):
     with pytest.raises(Z.ZeroError) as e:
         Z.zero_adam_step(plan, _good(plan, **over))
     assert e.value.code == code, Z.zero_last_error()
+
+
+def test_args_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror of zero_adam_args_t has the header's field offsets and
+    size (compiled with the host C compiler against include/zero_shard.h)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    fields = [f for f, _ in Z.zero_adam_args_t._fields_]
+    prog = ["#include <stdio.h>", "#include <stddef.h>", '#include "zero_shard.h"', "int main(void) {",
+            '  printf("%zu\\n", sizeof(zero_adam_args_t));']
+    prog += [f'  printf("%zu\\n", offsetof(zero_adam_args_t, {f}));' for f in fields]
+    prog += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(prog) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(Z.zero_adam_args_t)
+    for f, off in zip(fields, out[1:]):
+        assert getattr(Z.zero_adam_args_t, f).offset == off, f

@@ -8,8 +8,8 @@ import torch
 
 import workloads as W
 import zero_sharded_mixed_plan_amd as Z
-from gpu_harness import (CODE, Rig, check_params, compare_step, from_storage, guards, say,
-                         storage)
+from gpu_harness import (CODE, Rig, check_params, compare_step, from_storage, guards, round_up,
+                         say, storage)
 from oracle import casts as OC
 from oracle import plan as OP
 from oracle import step as OS
@@ -32,24 +32,46 @@ SEP, TILED = Z.ZERO_STATE_SEPARATE, Z.ZERO_STATE_TILED
 LAYOUTS = pytest.mark.parametrize("layout", [SEP, TILED], ids=["separate", "tiled"])
 
 
-def run_workload(w: W.Workload, ld_align=64, rank=None, steps=None, layout=SEP):
+def _grads(rig: Rig, source: str, step: int):
+    """One step's gradient: (device buffers, fused-call options, oracle slices).
+
+    slices: the N ranks' [S] contributions (the fused reduce-scatter);
+    stored: one stored [S] reduce-scatter output (row 0 of the slices);
+    full:   one full flat gradient read at the rank's slots (ZeRO-1);
+    full_n: N full flat gradients, summed in the step."""
+    w = rig.w
+    if source in ("slices", "stored"):
+        sl_cpu, sl_dev = rig.slices(step)
+        if source == "slices":
+            return sl_dev, {}, _oracle_slices(sl_cpu, rig.S, w.world)
+        return sl_dev, dict(count=1), [storage(sl_cpu[0, :rig.S])]
+    count = {"full": 1, "full_n": w.world}[source]
+    NS = rig.pl.padded_numel
+    ldf = round_up(NS, 64)
+    full = W.make_full_grads(w, NS, rig.lay.tensor_flat_off, count, step=step, ld=ldf)
+    sl = [OS.read_pieces(storage(full[k, :NS]), rig.lay.segments) for k in range(count)]
+    return full.to(rig.dev), dict(count=count, layout=Z.ZERO_GRAD_FULL, ld=ldf), sl
+
+
+def run_workload(w: W.Workload, ld_align=64, rank=None, steps=None, layout=SEP, source="slices"):
     """Run w.steps steps on the GPU and in the oracle; compare everything."""
     rig = Rig(w, ld_align=ld_align, rank=rank, layout=layout)
     w = rig.w
     say(f"workload {w.name} S={rig.S} N={w.world} rank={w.rank} grads={w.grad_dtype} "
-        f"params={w.param_dtype} buckets={len(rig.lay.segments)} ld={rig.ld} layout={layout}")
+        f"params={w.param_dtype} buckets={len(rig.lay.segments)} ld={rig.ld} layout={layout} "
+        f"source={source}")
     p, m, v = rig.p0, rig.m0, rig.v0
     gather_ref = rig.gather0.copy()
     cur, nxt = rig.A, rig.B
     t = w.t0
     same = total = 0
     for step in range(1, (steps or w.steps) + 1):
-        sl_cpu, sl_dev = rig.slices(step)
-        sl = _oracle_slices(sl_cpu, rig.S, w.world)
+        sl_dev, gkw, sl = _grads(rig, source, step)
         kw = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
                   t=t + 1, inv_scale=1.0 / w.loss_scale)
         if w.max_norm > 0:
-            rig.reduce_norm(sl_dev)
+            assert source in ("slices", "stored"), "the clipped path reads shard buffers"
+            rig.reduce_norm(sl_dev, count=gkw.get("count", 0))
             torch.cuda.synchronize()
             g_ref = OS.unscale(OS.average(OS.reduce_slices(sl, w.grad_dtype), w.world),
                                1.0 / w.loss_scale)
@@ -67,7 +89,7 @@ def run_workload(w: W.Workload, ld_align=64, rank=None, steps=None, layout=SEP):
                                 max_norm=w.max_norm, clip_override=c_gpu, **kw)
             out = cur
         else:
-            rig.fused(sl_dev, cur, nxt, t + 1)
+            rig.fused(sl_dev, cur, nxt, t + 1, **gkw)
             res = OS.shard_step(sl, w.grad_dtype, w.param_dtype, w.world, p, m, v, **kw)
             out = cur if res.flag else nxt
         torch.cuda.synchronize()
@@ -287,3 +309,73 @@ def test_norm_deterministic_and_partitioned():
     rig.reduce_norm(sl_dev, max_norm=1e6)
     torch.cuda.synchronize()
     assert rig.clip.item() == 1.0
+
+
+# ---------------------------------------------------------------------------
+# other gradient sources: a stored reduce-scatter output (one summed [S]
+# buffer) and a gradient all-reduced in full (ZeRO-1: full flat buffers read
+# at the rank's slots)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("world", [8, 64])
+@pytest.mark.parametrize("g", ["f32", "bf16", "f16"])
+def test_stored_rs_output(g, world):
+    p = "f32" if g == "f32" else "bf16"
+    ls = 1024.0 if g == "f16" else 1.0
+    run_workload(_flat(world * 5003, world, world - 1, g, p, loss_scale=ls), layout=TILED,
+                 source="stored")
+    run_workload(_flat(world * 5003, world, 1, g, p, loss_scale=ls, max_norm=0.01), layout=TILED,
+                 source="stored")
+
+
+def _ragged(world, rank, g, p, n_tensors, size, cap, seed=5):
+    """Tensors of odd sizes packed into buckets: pieces start at every alignment
+    in the full gradient, and vectors of 8 straddle piece boundaries."""
+    sizes = [size + 37 * (i % 5) for i in range(n_tensors)]
+    return W.Workload(name=f"ragged{n_tensors}x{size}_n{world}_r{rank}_{g}",
+                      tensors=tuple((f"t{i}", (n,)) for i, n in enumerate(sizes)), world=world,
+                      rank=rank, bucket_cap=cap, grad_dtype=g, param_dtype=p, lr=1e-3,
+                      weight_decay=0.05, steps=2, seed=seed)
+
+
+@pytest.mark.parametrize("source", ["full", "full_n"])
+@pytest.mark.parametrize("g,p", [("bf16", "bf16"), ("f16", "f16"), ("f32", "f32"), ("bf16", "f32")])
+@pytest.mark.parametrize("case", [
+    (4, 3, 7, 4099, 9000),      # a few buckets, S > 8192: the multi-workgroup update
+    (4, 1, 7, 999, 3000),       # S <= 8192 in one launch group: the one-workgroup path
+    (3, 2, 70, 97, 150),        # 70 buckets: several launch groups of at most 24 pieces
+    (8, 0, 1, 100_003, 0),      # one flat bucket, rank 0
+])
+def test_full_gradient(case, g, p, source):
+    world, rank, n, size, cap = case
+    for layout in (SEP, TILED):
+        run_workload(_ragged(world, rank, g, p, n, size, cap), layout=layout, source=source)
+
+
+@pytest.mark.parametrize("inside", [True, False])
+def test_full_gradient_overflow_only_in_own_pieces(inside):
+    """+inf in the full gradient flags the step only when it falls in this rank's
+    pieces; another rank's inf is not this rank's business."""
+    w = _ragged(4, 2, "bf16", "bf16", 7, 4099, 9000)
+    rig = Rig(w, layout=TILED)
+    segs = rig.lay.segments
+    goff, _lo, ln, _v = segs[1]
+    at = goff + ln // 2 if inside else (goff + ln + 5 if rig.w.rank < 3 else goff - 5)
+    NS = rig.pl.padded_numel
+    full = W.make_full_grads(w, NS, rig.lay.tensor_flat_off, 1, step=1, inf_at=at)
+    sl = [OS.read_pieces(storage(full[0, :NS]), segs)]
+    assert bool(np.isinf(OC.widen(sl[0], "bf16")).any()) == inside
+    rig.fused(full.to("cuda"), rig.A, rig.B, 1, count=1, layout=Z.ZERO_GRAD_FULL, ld=0)
+    torch.cuda.synchronize()
+    assert int(rig.flag.item()) == int(inside)
+    res = OS.shard_step(sl, "bf16", "bf16", w.world, rig.p0, rig.m0, rig.v0, lr=w.lr,
+                        weight_decay=w.weight_decay, t=1)
+    assert res.flag == inside
+    got = rig.unpack(rig.A if inside else rig.B)
+    if inside:
+        assert np.array_equal(got[0].view(np.uint32), rig.p0.view(np.uint32))
+    else:
+        assert np.array_equal(got[0].view(np.uint32), res.master.view(np.uint32))
+    gref = rig.gather0.copy()
+    OS.write_gather(gref, segs, res.params)
+    assert np.array_equal(rig.gather_np(), gref)

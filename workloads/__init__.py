@@ -178,6 +178,7 @@ def _gen(device, seed: int, stream: int):
 
 STREAM_MASTER, STREAM_M, STREAM_V, STREAM_SIGMA, STREAM_ZEROS, STREAM_INF = 1, 2, 3, 4, 5, 6
 STREAM_SLICE0 = 100  # slice k of step s uses STREAM_SLICE0 + 1000*s + k
+STREAM_FULL0 = 10_000_000  # full gradient k of step s uses STREAM_FULL0 + 1000*s + k
 
 
 def tensor_sigmas(w: Workload) -> List[float]:
@@ -311,4 +312,29 @@ def make_slices(w: Workload, lay: Layout, step: int = 1, ld: Optional[int] = Non
     if w.inject_inf_step is not None and step == w.inject_inf_step:
         k, j = inf_position(w, S)
         out[k, j] = float("inf")
+    return out
+
+
+def make_full_grads(w: Workload, padded: int, tensor_offsets: Sequence[int], count: int,
+                    step: int = 1, ld: Optional[int] = None, device="cpu", inf_at: Optional[int] = None):
+    """count whole flat gradients [count, ld] in w.grad_dtype, each laid out like
+    the padded flat parameter vector (tensor i at tensor_offsets[i]): entries of
+    tensor i ~ N(0, sigma_i) * loss_scale, padding and columns >= padded are +0.
+    inf_at, if given, puts +inf at that flat index of buffer 0."""
+    import torch
+    ld = padded if ld is None else ld
+    assert ld >= padded
+    out = torch.zeros((count, ld), dtype=torch_dtype(w.grad_dtype), device=device)
+    sig = tensor_sigmas(w)
+    sizes = numels(w.tensors)
+    for k in range(count):
+        g = _gen(device, w.seed, STREAM_FULL0 + 1000 * step + k)
+        x = torch.randn(padded, generator=g, device=device, dtype=torch.float32)
+        y = torch.zeros(padded, dtype=torch.float32, device=device)
+        for i, n in enumerate(sizes):
+            o = tensor_offsets[i]
+            y[o:o + n] = x[o:o + n] * (sig[i] * w.loss_scale)
+        out[k, :padded].copy_(y)
+    if inf_at is not None:
+        out[0, inf_at] = float("inf")
     return out

@@ -7,14 +7,15 @@ on first use (any planner or device call), which fails loudly if it has not been
 built; nothing here falls back to another implementation.
 """
 from ._abi import (DTYPE_BYTES, DTYPE_CODES, EXPORTS, ZERO_BF16, ZERO_EALIGN, ZERO_EHIP,
-                   ZERO_EINVAL, ZERO_ENOMEM, ZERO_F16, ZERO_F32, ZERO_OK, ZERO_STATE_SEPARATE,
+                   ZERO_EINVAL, ZERO_ENOMEM, ZERO_F16, ZERO_F32, ZERO_GRAD_FULL, ZERO_GRAD_SHARD, ZERO_OK,
+                   ZERO_STATE_SEPARATE,
                    ZERO_STATE_TILE, ZERO_STATE_TILED, Plan, ZeroError,
                    adam_args, lib, zero_adam_args_t, zero_adam_step, zero_last_error,
                    zero_reduce_shard, zero_shard_norm, zero_version)
 
 __all__ = [
     "DTYPE_BYTES", "DTYPE_CODES", "EXPORTS", "ZERO_BF16", "ZERO_EALIGN", "ZERO_EHIP", "ZERO_EINVAL",
-    "ZERO_ENOMEM", "ZERO_F16", "ZERO_F32", "ZERO_OK", "ZERO_STATE_SEPARATE", "ZERO_STATE_TILE",
+    "ZERO_ENOMEM", "ZERO_F16", "ZERO_F32", "ZERO_GRAD_FULL", "ZERO_GRAD_SHARD", "ZERO_OK", "ZERO_STATE_SEPARATE", "ZERO_STATE_TILE",
     "ZERO_STATE_TILED", "Plan", "ZeroError", "adam_args", "lib",
     "zero_adam_args_t", "zero_adam_step", "zero_last_error", "zero_reduce_shard",
     "zero_shard_norm", "zero_version",

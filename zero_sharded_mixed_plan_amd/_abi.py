@@ -18,6 +18,7 @@ ZERO_OK, ZERO_EINVAL, ZERO_EALIGN, ZERO_ENOMEM, ZERO_EHIP = 0, -1, -2, -3, -4
 ZERO_F32, ZERO_BF16, ZERO_F16 = 0, 1, 2
 ZERO_STATE_SEPARATE, ZERO_STATE_TILED = 0, 1
 ZERO_STATE_TILE = 2048
+ZERO_GRAD_SHARD, ZERO_GRAD_FULL = 0, 1
 DTYPE_CODES = {"f32": ZERO_F32, "bf16": ZERO_BF16, "f16": ZERO_F16}
 DTYPE_BYTES = {ZERO_F32: 4, ZERO_BF16: 2, ZERO_F16: 2}
 
@@ -43,6 +44,8 @@ class zero_adam_args_t(ctypes.Structure):
         ("grad", ctypes.c_void_p),
         ("grad_ld", ctypes.c_int64),
         ("grad_dtype", ctypes.c_int),
+        ("grad_count", ctypes.c_int32),
+        ("grad_layout", ctypes.c_int32),
         ("inv_scale", ctypes.c_float),
         ("g_stash", ctypes.c_void_p),
         ("clip_coef", ctypes.c_void_p),
@@ -105,7 +108,7 @@ def load(path: str) -> ctypes.CDLL:
         "zero_plan_bytes": (ctypes.c_int, [vp, i32, ctypes.POINTER(f64), P64]),
         "zero_state_numel": (i64, [vp, i32]),
         "zero_workspace_bytes": (ctypes.c_size_t, [vp]),
-        "zero_reduce_shard": (ctypes.c_int, [vp, vp, i64, ctypes.c_int, f32, vp, vp, i32, vp]),
+        "zero_reduce_shard": (ctypes.c_int, [vp, vp, i64, i32, ctypes.c_int, f32, vp, vp, i32, vp]),
         "zero_shard_norm": (ctypes.c_int, [vp, vp, f64, f64, vp, vp, vp, vp]),
         "zero_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(zero_adam_args_t), vp]),
         "zero_last_error": (ctypes.c_char_p, []),
@@ -232,9 +235,12 @@ class Plan:
 # ---------------------------------------------------------------------------
 
 def zero_reduce_shard(plan: Plan, grad: int, grad_ld: int, grad_dtype: int, inv_scale: float,
-                      g_out: int, ws: int, want_sumsq: bool, stream: int = 0) -> None:
-    _check(lib().zero_reduce_shard(plan.handle, grad, grad_ld, grad_dtype, inv_scale, g_out or None,
-                                   ws, 1 if want_sumsq else 0, stream or None))
+                      g_out: int, ws: int, want_sumsq: bool, stream: int = 0,
+                      grad_count: int = 0) -> None:
+    """grad_count: gradient buffers summed (0 = N, one per rank; 1 = a stored
+    reduce-scatter output)."""
+    _check(lib().zero_reduce_shard(plan.handle, grad, grad_ld, grad_count, grad_dtype, inv_scale,
+                                   g_out or None, ws, 1 if want_sumsq else 0, stream or None))
 
 
 def zero_shard_norm(plan: Plan, ws: int, other_ranks_sumsq: float, max_norm: float,

@@ -50,15 +50,30 @@ Range rng(const void* p, int64_t bytes, const char* name) {
   return Range{a, a + (uintptr_t)bytes, name};
 }
 
-// Slice dtype/stride checks shared by the fused step and the reduce pass.
-int check_slices(const char* fn, const void* grad, int64_t ld, zero_dtype_t gt, int64_t S) {
+// Gradient-buffer checks shared by the fused step and the reduce pass.  count
+// buffers of `len` elements each (the shard, or the full padded vector); the
+// stride matters only when there are several.  Shard buffers start on 16-byte
+// boundaries; full buffers need element alignment (each vector's alignment is
+// checked in the kernel).
+int check_grad(const char* fn, const void* grad, int64_t ld, int32_t count, zero_dtype_t gt, bool full,
+               int64_t len) {
   const int gb = dtype_bytes(gt);
   if (gb == 0) return fail(ZERO_EINVAL, std::string(fn) + ": unsupported gradient dtype");
   if (!grad) return fail(ZERO_EINVAL, std::string(fn) + ": grad is NULL");
-  if (ld < S) return fail(ZERO_EINVAL, std::string(fn) + ": grad_ld is smaller than the shard");
-  if (!aligned(grad, 16) || (ld * gb) % 16 != 0)
-    return fail(ZERO_EALIGN, std::string(fn) + ": slices must start on 16-byte boundaries");
+  if (count < 1) return fail(ZERO_EINVAL, std::string(fn) + ": grad_count must be >= 0 (0 = N)");
+  if (count > 1 && ld < len)
+    return fail(ZERO_EINVAL, std::string(fn) + ": grad_ld is smaller than one gradient buffer");
+  if (count > 1 && (ld * gb) % 16 != 0)
+    return fail(ZERO_EALIGN, std::string(fn) + ": grad_ld must be a multiple of 16 bytes");
+  if (!aligned(grad, full ? (uintptr_t)gb : 16))
+    return fail(ZERO_EALIGN, std::string(fn) + (full ? ": grad is not element aligned"
+                                                     : ": slices must start on 16-byte boundaries"));
   return ZERO_OK;
+}
+
+// bytes spanned by the gradient buffers
+int64_t grad_span(int64_t ld, int32_t count, int64_t len, int gb) {
+  return ((int64_t)(count - 1) * ld + len) * gb;
 }
 
 void slice_consts(int32_t n, int32_t* n_pow2, float* nf, float* recip) {
@@ -70,27 +85,28 @@ void slice_consts(int32_t n, int32_t* n_pow2, float* nf, float* recip) {
 }  // namespace
 
 extern "C" int zero_reduce_shard(const zero_plan_t* plan, const void* grad, int64_t grad_ld,
-                                 zero_dtype_t grad_dtype, float inv_scale, float* g_out, void* ws,
-                                 int32_t want_sumsq, void* stream) {
+                                 int32_t grad_count, zero_dtype_t grad_dtype, float inv_scale, float* g_out,
+                                 void* ws, int32_t want_sumsq, void* stream) {
   if (!plan) return fail(ZERO_EINVAL, "zero_reduce_shard: plan is NULL");
   if (!ws) return fail(ZERO_EINVAL, "zero_reduce_shard: workspace is NULL");
   if (!aligned(ws, 16)) return fail(ZERO_EALIGN, "zero_reduce_shard: workspace must be 16-byte aligned");
   const int64_t S = plan->shard;
-  int rc = check_slices("zero_reduce_shard", grad, grad_ld, grad_dtype, S);
+  if (grad_count < 0) return fail(ZERO_EINVAL, "zero_reduce_shard: grad_count must be >= 0 (0 = N)");
+  const int32_t count = grad_count == 0 ? plan->world : grad_count;
+  int rc = check_grad("zero_reduce_shard", grad, grad_ld, count, grad_dtype, false, S);
   if (rc) return rc;
   if (g_out && !aligned(g_out, 16)) return fail(ZERO_EALIGN, "zero_reduce_shard: g_out must be 16-byte aligned");
   if (!std::isfinite(inv_scale)) return fail(ZERO_EINVAL, "zero_reduce_shard: inv_scale is not finite");
   if (g_out) {
-    const int gb = dtype_bytes(grad_dtype);
-    const Range gr = rng(grad, ((int64_t)(plan->world - 1) * grad_ld + S) * gb, "grad");
+    const Range gr = rng(grad, grad_span(grad_ld, count, S, dtype_bytes(grad_dtype)), "grad");
     if (overlaps(gr, rng(g_out, S * 4, "g_out")))
       return fail(ZERO_EINVAL, "zero_reduce_shard: g_out overlaps the slices");
   }
   zk::ReduceLaunch a{};
   a.grad = grad;
-  a.ld_bytes = grad_ld * dtype_bytes(grad_dtype);
-  a.n = plan->world;
-  slice_consts(a.n, &a.n_pow2, &a.nf, &a.recip_n);
+  a.ld_bytes = count > 1 ? grad_ld * dtype_bytes(grad_dtype) : 0;
+  a.n = count;
+  slice_consts(plan->world, &a.n_pow2, &a.nf, &a.recip_n);
   a.inv_scale = inv_scale;
   a.g_out = g_out;
   a.ws_flags = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + zk::ws_flags_offset(S));
@@ -137,6 +153,9 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
   const int32_t N = plan->world;
   if (A.rank < 0 || A.rank >= N) return fail(ZERO_EINVAL, "zero_adam_step: rank out of range");
   const bool stash = A.g_stash != nullptr;
+  const int32_t count = A.grad_count == 0 ? N : A.grad_count;
+  const bool full = A.grad_layout == ZERO_GRAD_FULL;
+  const int64_t glen = full ? plan->padded : S;  // elements of one gradient buffer
   const int pb = dtype_bytes(A.param_dtype);
   if (pb == 0) return fail(ZERO_EINVAL, "zero_adam_step: unsupported parameter dtype");
 
@@ -163,7 +182,10 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
     if (!aligned(A.g_stash, 16)) return fail(ZERO_EALIGN, "zero_adam_step: g_stash must be 16-byte aligned");
     if (A.clip_coef && !aligned(A.clip_coef, 4)) return fail(ZERO_EALIGN, "zero_adam_step: clip_coef misaligned");
   } else {
-    const int rc = check_slices("zero_adam_step", A.grad, A.grad_ld, A.grad_dtype, S);
+    if (A.grad_layout != ZERO_GRAD_SHARD && A.grad_layout != ZERO_GRAD_FULL)
+      return fail(ZERO_EINVAL, "zero_adam_step: unknown gradient layout");
+    if (A.grad_count < 0) return fail(ZERO_EINVAL, "zero_adam_step: grad_count must be >= 0 (0 = N)");
+    const int rc = check_grad("zero_adam_step", A.grad, A.grad_ld, count, A.grad_dtype, full, glen);
     if (rc) return rc;
     if (!std::isfinite(A.inv_scale)) return fail(ZERO_EINVAL, "zero_adam_step: inv_scale is not finite");
   }
@@ -194,7 +216,7 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
   if (stash)
     in_r.push_back(rng(A.g_stash, S * 4, "g_stash"));
   else
-    in_r.push_back(rng(A.grad, ((int64_t)(N - 1) * A.grad_ld + S) * dtype_bytes(A.grad_dtype), "grad"));
+    in_r.push_back(rng(A.grad, grad_span(A.grad_ld, count, glen, dtype_bytes(A.grad_dtype)), "grad"));
   const bool strict = !stash && A.overflow_out != nullptr;
   for (size_t i = 0; i < in_r.size(); ++i) {
     for (size_t j = 0; j < out_r.size(); ++j) {
@@ -221,8 +243,9 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
     return fail(ZERO_EINVAL, "zero_adam_step: bias correction rounds to 0 in fp32");
 
   L.grad = A.grad;
-  L.ld_bytes = stash ? 0 : A.grad_ld * dtype_bytes(A.grad_dtype);
-  L.n = N;
+  L.ld_bytes = (stash || count == 1) ? 0 : A.grad_ld * dtype_bytes(A.grad_dtype);
+  L.grad_full = (!stash && full) ? 1 : 0;
+  L.n = stash ? N : count;
   slice_consts(N, &L.n_pow2, &L.nf, &L.recip_n);
   L.inv_scale = A.inv_scale;
   L.g_stash = A.g_stash;

@@ -332,6 +332,31 @@ __device__ __forceinline__ int64_t delta_of(const StepLaunch& a, int64_t j) {
   return d;
 }
 
+// Slice sum for 8 local elements whose gradient sits in full flat buffers at
+// the gather offsets (the gradient all-reduced in full): one aligned vector
+// per buffer when the 8 fall in one piece on a 16-byte boundary, else element
+// by element (a piece boundary inside the 8, or a slot that is not 16-byte
+// aligned).
+template <class GT, int NB>
+__device__ __forceinline__ void reduce8_pieces(const StepLaunch& a, int64_t j0, float acc[8]) {
+  const char* g = static_cast<const char*>(a.grad);
+  const int64_t d0 = delta_of(a, j0);
+  const char* p = g + (j0 + d0) * GT::bytes;
+  if (delta_of(a, j0 + kVec - 1) == d0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+    reduce8<GT, NB>(p, a.ld_bytes, a.n, acc);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      acc[e] = reduce1<GT>(g + (j0 + e + delta_of(a, j0 + e)) * GT::bytes, a.ld_bytes, a.n);
+  }
+}
+
+// the gradient of local element j in slice 0
+template <class GT>
+__device__ __forceinline__ const char* grad_elem(const StepLaunch& a, int64_t j) {
+  return static_cast<const char*>(a.grad) + (j + (a.grad_full ? delta_of(a, j) : 0)) * GT::bytes;
+}
+
 // ---------------------------------------------------------------------------
 // the update kernel (fused: N slices in; stash: fp32 g in)
 // ---------------------------------------------------------------------------
@@ -376,7 +401,8 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
                                       load_state);
       } else {
         load_state();
-        reduce8<GT, NB>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes, a.n, acc);
+        if (a.grad_full) reduce8_pieces<GT, NB>(a, j0, acc);
+        else reduce8<GT, NB>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes, a.n, acc);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -406,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
       if (STASH) {
         ge = a.g_stash[j] * clip;
       } else {
-        const float acc = reduce1<GT>(static_cast<const char*>(a.grad) + j * GT::bytes, a.ld_bytes, a.n);
+        const float acc = reduce1<GT>(grad_elem<GT>(a, j), a.ld_bytes, a.n);
         ge = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, a.inv_scale);
         bad |= !__builtin_isfinite(ge);
       }
@@ -440,15 +466,18 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
   bool bad = false;
   if (cnt == kVec) {
     float acc[8];
-    reduce8<GT, Batch<GT, false>::value>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes,
-                                         a.n, acc);
+    if (a.grad_full)
+      reduce8_pieces<GT, Batch<GT, false>::value>(a, j0, acc);
+    else
+      reduce8<GT, Batch<GT, false>::value>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes,
+                                           a.n, acc);
 #pragma unroll
     for (int e = 0; e < 8; ++e) g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, a.inv_scale);
   } else {
     for (int e = 0; e < 8; ++e) {
       g[e] = 0.0f;
       if (e < cnt) {
-        const float acc = reduce1<GT>(static_cast<const char*>(a.grad) + (j0 + e) * GT::bytes, a.ld_bytes, a.n);
+        const float acc = reduce1<GT>(grad_elem<GT>(a, j0 + e), a.ld_bytes, a.n);
         g[e] = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, a.inv_scale);
       }
     }
@@ -672,7 +701,7 @@ int launch_fill_u32(u32* p, u32 value, void* stream) {
 template <class GT, class PT, bool STASH, bool WIDE>
 static void go_step_full(const StepLaunch& a, unsigned blocks, size_t lds, hipStream_t st) {
   constexpr int NB = Batch<GT, WIDE>::value;
-  const int nbatch = (!STASH && a.n % NB == 0) ? a.n / NB : 0;
+  const int nbatch = (!STASH && !a.grad_full && a.n % NB == 0) ? a.n / NB : 0;
   const dim3 g(blocks), b(kThreads);
   switch (nbatch) {
     case 1: hipLaunchKernelGGL((step_kernel<GT, PT, STASH, WIDE, 1>), g, b, lds, st, a); return;

@@ -57,9 +57,10 @@ struct StepLaunch {
   // gradient source
   const void* grad;
   int64_t ld_bytes;       // slice stride in bytes
-  int32_t n;              // N
-  int32_t n_pow2;         // N is a power of two: acc * (1/N) is the IEEE quotient
-  float nf;               // float(N)
+  int32_t grad_full;      // slices are full flat gradients read at the gather offsets
+  int32_t n;              // slices summed
+  int32_t n_pow2;         // the divisor N is a power of two: acc * (1/N) is the IEEE quotient
+  float nf;               // float(N), N = the world size
   float recip_n;          // 1/N (exact when n_pow2)
   float inv_scale;
   const float* g_stash;   // stash mode when non-null
@@ -88,7 +89,7 @@ struct StepLaunch {
 struct ReduceLaunch {
   const void* grad;
   int64_t ld_bytes;
-  int32_t n;
+  int32_t n;              // slices summed (the divisor is the world size, in nf)
   int32_t n_pow2;
   float nf, recip_n, inv_scale;
   float* g_out;
