@@ -121,14 +121,28 @@ def cpu_baseline(w, slices, tiled_state, S, target_s=12.0, max_elems=1 << 26, ch
 # one workload on the GPU
 # ---------------------------------------------------------------------------
 
+# Other gradient sources of the same step, on the GPT-2 shard (extra lines of
+# --workload all): one stored reduce-scatter output read in place of the N
+# slices, one full all-reduced gradient read at the rank's slots (ZeRO-1), and
+# the clipped path's reduction pass alone.
+VARIANTS = {
+    "gpt2_1p5b_n8_stored_rs": ("gpt2_1p5b_n8", "stored"),
+    "gpt2_1p5b_n8_zero1_full": ("gpt2_1p5b_n8", "full"),
+    "gpt2_1p5b_n8_reduce_only": ("gpt2_1p5b_n8", "reduce_only"),
+}
+
+
 def run(name, steps, warmup, with_cpu):
+    import dataclasses
+
     import torch
 
     import workloads as W
     import zero_sharded_mixed_plan_amd as Z
     from zero_sharded_mixed_plan_amd.optim import dtype_code, pack_state, state_arg_dict
 
-    w = W.FULL[name]
+    base, source = VARIANTS.get(name, (name, "slices"))
+    w = W.FULL[base]
     layout = Z.ZERO_STATE_TILED
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -140,9 +154,18 @@ def run(name, steps, warmup, with_cpu):
         f"grads={w.grad_dtype} params={w.param_dtype} clip={w.max_norm}")
 
     t_gen = time.perf_counter()
-    slices = W.make_slices(w, lay, step=1, ld=ld, device=dev)
-    if w.inject_inf_step is not None:   # time clean steps: draw the slices of a clean step
-        slices = W.make_slices(w, lay, step=w.inject_inf_step + 1, ld=ld, device=dev, out=slices)
+    count, glayout, gld = 0, Z.ZERO_GRAD_SHARD, ld
+    if source == "stored":        # one [S] buffer holding the summed gradient
+        slices = W.make_slices(dataclasses.replace(w, world=1), lay, step=1, ld=ld, device=dev)
+        count, gld = 1, 0
+    elif source == "full":        # one full flat gradient [padded]
+        slices = W.make_full_grads(w, plan.padded_numel, plan.tensor_offsets(), 1, step=1, device=dev)
+        count, glayout, gld = 1, Z.ZERO_GRAD_FULL, 0
+    else:
+        slices = W.make_slices(w, lay, step=1, ld=ld, device=dev)
+        if w.inject_inf_step is not None:   # time clean steps: draw the slices of a clean step
+            slices = W.make_slices(w, lay, step=w.inject_inf_step + 1, ld=ld, device=dev, out=slices)
+    n_read = w.world if count == 0 else count   # gradient buffers each step reads
     p0, m0, v0 = W.make_state(w, lay, dev)
     A = [pack_state(p0, m0, v0, plan.state_numel(layout))]
     del p0, m0, v0
@@ -150,7 +173,8 @@ def run(name, steps, warmup, with_cpu):
     gather = torch.zeros(plan.padded_numel, dtype=W.torch_dtype(w.param_dtype), device=dev)
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     clip = w.max_norm > 0
-    if clip:
+    reduce_only = source == "reduce_only"
+    if clip or reduce_only:
         g = torch.empty(S, dtype=torch.float32, device=dev)
         ws = torch.empty(plan.workspace_bytes(), dtype=torch.uint8, device=dev)
         sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
@@ -175,7 +199,15 @@ def run(name, steps, warmup, with_cpu):
 
     def step(ev=None):
         t = state["t"] + 1
-        if clip:
+        if reduce_only:
+            e0, e1 = ev if ev else (None, None)
+            if e0 is not None:
+                e0.record(stream)
+            Z.zero_reduce_shard(plan, slices.data_ptr(), ld, dtype_code(slices.dtype),
+                                1.0 / w.loss_scale, g.data_ptr(), ws.data_ptr(), True, st)
+            if e1 is not None:
+                e1.record(stream)
+        elif clip:
             e_red0, e_red1, e_up0, e_up1 = ev if ev else (None,) * 4
             if e_red0 is not None:
                 e_red0.record(stream)
@@ -194,7 +226,8 @@ def run(name, steps, warmup, with_cpu):
         else:
             e0, e1 = ev if ev else (None, None)
             src, dst = state["cur"], state["nxt"]
-            a = Z.adam_args(grad=slices.data_ptr(), grad_ld=ld, grad_dtype=dtype_code(slices.dtype),
+            a = Z.adam_args(grad=slices.data_ptr(), grad_ld=gld, grad_dtype=dtype_code(slices.dtype),
+                            grad_count=count, grad_layout=glayout,
                             inv_scale=1.0 / w.loss_scale, overflow_out=flag.data_ptr(), step=t,
                             ev_begin=e0.cuda_event if e0 else None,
                             ev_end=e1.cuda_event if e1 else None,
@@ -210,7 +243,7 @@ def run(name, steps, warmup, with_cpu):
     if int(flag.item()) != 0:
         raise RuntimeError("warm-up step overflowed on finite synthetic data")
 
-    n_ev = 4 if clip else 2
+    n_ev = 4 if (clip and not reduce_only) else 2
     evs = [new_events(n_ev) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -223,18 +256,23 @@ def run(name, steps, warmup, with_cpu):
 
     ms_step = wall / steps * 1e3
     kernels = {}
-    if clip:
+    if reduce_only:
+        red = [evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)]
+        kernels["reduce_kernel"] = (sum(red) / steps, w.world * gb + 4)
+        bpe_total = w.world * gb + 4
+    elif clip:
         red = [evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)]
         upd = [evs[i][2].elapsed_time(evs[i][3]) for i in range(steps)]
         kernels["reduce_kernel"] = (sum(red) / steps, w.world * gb + 4)
         kernels["step_kernel_stash"] = (sum(upd) / steps, 4 + 24 + pb)
+        bpe_total = w.world * gb + 24 + pb + 8
     else:
         upd = [evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)]
-        kernels["step_kernel"] = (sum(upd) / steps, w.world * gb + 24 + pb)
+        kernels["step_kernel"] = (sum(upd) / steps, n_read * gb + 24 + pb)
+        bpe_total = n_read * gb + 24 + pb
     dom = max(kernels, key=lambda k: kernels[k][0])
     k_ms, k_bpe = kernels[dom]
     achieved = k_bpe * S / (k_ms * 1e-3) / 1e9
-    bpe_total = w.world * gb + 24 + pb + (8 if clip else 0)
     traffic = load_traffic(dom, name)
     out = {
         "metric": METRIC,
@@ -250,9 +288,14 @@ def run(name, steps, warmup, with_cpu):
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": name, "shard_elements": S, "world": w.world, "rank": w.rank,
+            "workload": name, "gradient_source": {"slices": "N slices (fused reduce-scatter)",
+                                                  "stored": "one stored reduce-scatter output",
+                                                  "full": "one full all-reduced gradient (ZeRO-1)",
+                                                  "reduce_only": "N slices, reduction pass alone"}[source],
+            "shard_elements": S, "world": w.world, "rank": w.rank,
             "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype, "buckets": plan.num_buckets,
-            "clip": clip, "state_layout": "tiled", "algorithmic_bytes_per_element": bpe_total,
+            "clip": clip and not reduce_only, "state_layout": "tiled",
+            "algorithmic_bytes_per_element": bpe_total,
             "step_GBps": bpe_total * S / (ms_step * 1e-3) / 1e9,
             "kernel_ms": {k: round(v[0], 5) for k, v in kernels.items()},
             "parallelism": "one rank of N (single GPU)",
@@ -322,9 +365,9 @@ def main():
         log("[bench] copy calibration: 3 x torch.neg over 2^28 fp32 (1 GiB read + 1 GiB written)")
         del src, dst
     import workloads as W
-    names = W.ORDER if args.workload == "all" else [args.workload]
-    if args.workload != "all" and args.workload not in W.FULL:
-        sys.exit(f"unknown workload {args.workload}; one of {W.ORDER} or 'all'")
+    names = W.ORDER + list(VARIANTS) if args.workload == "all" else [args.workload]
+    if args.workload != "all" and args.workload not in W.FULL and args.workload not in VARIANTS:
+        sys.exit(f"unknown workload {args.workload}; one of {W.ORDER + list(VARIANTS)} or 'all'")
     lines = {}
     for nm in names:
         res = run(nm, args.steps, args.warmup, with_cpu=(not args.no_cpu and nm == DEFAULT))
