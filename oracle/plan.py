@@ -101,6 +101,72 @@ def make_plan(numels: Sequence[int], world: int, bucket_cap: int = 0) -> Plan:
                 tensor_bucket=tuple(tensor_bucket), tensor_offset=tuple(tensor_offset))
 
 
+def make_plan_dim0(shapes: Sequence[Sequence[int]], world: int) -> Plan:
+    """Per-parameter dim-0 layout (FSDP2 fully_shard: every parameter a tensor
+    split on its first dimension; handbook chapter, section "ZeRO-3 与 FSDP").
+
+    Each parameter of shape (rows, *rest) is its own bucket.  Its rows are padded
+    to N * c with c = ceil(rows / N), rank r holding rows [r*c, (r+1)*c): S_b =
+    c * prod(rest), P_b = N * S_b, and the bucket in the gather buffer is the
+    padded parameter in row-major order.  A 0-d parameter counts as one row of
+    one element.  A parameter with no elements adds no bucket: it sits, empty, at
+    the end of the previous parameter's bucket (or the start of the next one).
+    The generic rank_segments then gives each rank one piece per parameter.
+    """
+    if world < 1:
+        raise ValueError("world size must be >= 1")
+    rows, row_numel = [], []
+    for sh in shapes:
+        sh = tuple(int(x) for x in sh)
+        if any(x < 0 for x in sh):
+            raise ValueError("negative dimension")
+        r = sh[0] if sh else 1
+        k = 1
+        for x in sh[1:]:
+            k *= x
+        rows.append(r)
+        row_numel.append(k)
+    numels = tuple(r * k for r, k in zip(rows, row_numel))
+    if len(numels) == 0 or sum(numels) == 0:
+        raise ValueError("need at least one element")
+    # groups: each non-empty parameter opens one; empty ones join the open group
+    groups: List[List[int]] = []
+    for i, n in enumerate(numels):
+        if n > 0 or not groups:
+            groups.append([i])
+        else:
+            groups[-1].append(i)
+    if numels[groups[0][0]] == 0:          # leading empties: merge into the first real group
+        lead = groups.pop(0)
+        groups[0] = lead + groups[0]
+    buckets: List[Bucket] = []
+    tensor_bucket = [0] * len(numels)
+    tensor_offset = [0] * len(numels)
+    base = 0
+    for b, idx in enumerate(groups):
+        main = [i for i in idx if numels[i] > 0][0]
+        shard = ceil_div(rows[main], world) * row_numel[main]
+        for i in idx:
+            tensor_bucket[i] = b
+            tensor_offset[i] = base + (numels[main] if i > main else 0)
+        buckets.append(Bucket(first_tensor=idx[0], n_tensors=len(idx), numel=numels[main],
+                              shard=shard, padded=world * shard, base=base))
+        base += world * shard
+    return Plan(world=world, numels=numels, buckets=tuple(buckets),
+                tensor_bucket=tuple(tensor_bucket), tensor_offset=tuple(tensor_offset))
+
+
+def dim0_local_shape(shape: Sequence[int], world: int, rank: int) -> Tuple[int, ...]:
+    """Shape of rank r's local shard of a dim-0 sharded parameter: rows
+    clamp(rows - r*c, 0, c) of c = ceil(rows / N), the rest unchanged (what
+    fully_shard's to_local() returns; the padding rows are not part of it)."""
+    shape = tuple(int(x) for x in shape)
+    rows = shape[0] if shape else 1
+    c = ceil_div(rows, world)
+    mine = min(max(rows - rank * c, 0), c)
+    return (mine,) + shape[1:] if shape else ((1,) if mine else (0,))
+
+
 def rank_segments(plan: Plan, rank: int) -> List[Tuple[int, int, int, int]]:
     """Rank r's pieces, one per bucket: (gather_off, local_off, seg_len, valid).
 
