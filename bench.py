@@ -121,14 +121,16 @@ def cpu_baseline(w, slices, tiled_state, S, target_s=12.0, max_elems=1 << 26, ch
 # one workload on the GPU
 # ---------------------------------------------------------------------------
 
-# Other gradient sources of the same step, on the GPT-2 shard (extra lines of
-# --workload all): one stored reduce-scatter output read in place of the N
-# slices, one full all-reduced gradient read at the rank's slots (ZeRO-1), and
-# the clipped path's reduction pass alone.
+# Other forms of the same step on the GPT-2 shard (extra lines of --workload
+# all): one stored reduce-scatter output read in place of the N slices, one
+# full all-reduced gradient read at the rank's slots (ZeRO-1), the clipped
+# path's reduction pass alone, and the per-parameter dim-0 layout (FSDP2
+# fully_shard: 580 pieces, one per parameter).
 VARIANTS = {
-    "gpt2_1p5b_n8_stored_rs": ("gpt2_1p5b_n8", "stored"),
-    "gpt2_1p5b_n8_zero1_full": ("gpt2_1p5b_n8", "full"),
-    "gpt2_1p5b_n8_reduce_only": ("gpt2_1p5b_n8", "reduce_only"),
+    "gpt2_1p5b_n8_stored_rs": ("gpt2_1p5b_n8", "stored", "flat"),
+    "gpt2_1p5b_n8_zero1_full": ("gpt2_1p5b_n8", "full", "flat"),
+    "gpt2_1p5b_n8_reduce_only": ("gpt2_1p5b_n8", "reduce_only", "flat"),
+    "gpt2_1p5b_n8_fsdp2_dim0": ("gpt2_1p5b_n8", "slices", "dim0"),
 }
 
 
@@ -141,12 +143,16 @@ def run(name, steps, warmup, with_cpu):
     import zero_sharded_mixed_plan_amd as Z
     from zero_sharded_mixed_plan_amd.optim import dtype_code, pack_state, state_arg_dict
 
-    base, source = VARIANTS.get(name, (name, "slices"))
+    base, source, plan_layout = VARIANTS.get(name, (name, "slices", "flat"))
     w = W.FULL[base]
     layout = Z.ZERO_STATE_TILED
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    plan = Z.Plan(W.numels(w.tensors), w.world, w.bucket_cap)
+    if plan_layout == "dim0":
+        w = dataclasses.replace(w, plan_layout="dim0")
+        plan = Z.Plan.dim0([shape for _n, shape in w.tensors], w.world)
+    else:
+        plan = Z.Plan(W.numels(w.tensors), w.world, w.bucket_cap)
     S = plan.shard_numel
     lay = W.Layout(S=S, segments=plan.segments(w.rank), tensor_flat_off=plan.tensor_offsets())
     ld = round_up(S, 64)
@@ -292,6 +298,7 @@ def run(name, steps, warmup, with_cpu):
                                                   "stored": "one stored reduce-scatter output",
                                                   "full": "one full all-reduced gradient (ZeRO-1)",
                                                   "reduce_only": "N slices, reduction pass alone"}[source],
+            "plan_layout": {"flat": "flat buckets", "dim0": "per-parameter dim-0 (FSDP2)"}[plan_layout],
             "shard_elements": S, "world": w.world, "rank": w.rank,
             "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype, "buckets": plan.num_buckets,
             "clip": clip and not reduce_only, "state_layout": "tiled",

@@ -91,6 +91,27 @@ typedef struct zero_plan zero_plan_t;
 int zero_plan(const int64_t* numel, int32_t n_tensors, int32_t world, int64_t bucket_cap,
               zero_plan_t** out);
 
+/*
+ * Per-parameter dim-0 layout (FSDP2 fully_shard: every parameter a tensor
+ * split on its first dimension; handbook chapter "ZeRO 与 FSDP：切分优化器状态、
+ * 梯度与参数", section "ZeRO-3 与 FSDP", where a (256, 64) weight on 2 ranks is
+ * held as (128, 64) per rank).
+ *
+ * Parameter i has rows[i] rows of row_numel[i] elements (a 0-d parameter: one
+ * row of one element).  Each parameter with elements is its own bucket: its
+ * rows are padded to N * c_i, c_i = ceil(rows[i] / N), so S_b = c_i *
+ * row_numel[i], P_b = N * S_b, rank r's piece holds rows [r*c_i, (r+1)*c_i),
+ * and the bucket in the gather buffer is the padded parameter in row-major
+ * order.  A parameter with no elements adds no bucket (it sits, empty, at the
+ * end of the previous parameter's bucket, or at the start of the next one).
+ * Every other call takes the plan as it takes a zero_plan() plan.
+ *
+ * rows, row_numel: host arrays, each >= 0, some parameter non-empty.  world >= 1.
+ * Errors: ZERO_EINVAL (bad sizes), ZERO_ENOMEM.
+ */
+int zero_plan_dim0(const int64_t* rows, const int64_t* row_numel, int32_t n_tensors, int32_t world,
+                   zero_plan_t** out);
+
 /* Free a plan (NULL is ignored). */
 void zero_plan_free(zero_plan_t* plan);
 

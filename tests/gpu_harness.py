@@ -39,9 +39,18 @@ def from_storage(a: np.ndarray, kind: str) -> torch.Tensor:
 
 
 def oracle_layout(w: W.Workload):
-    pl = OP.make_plan(W.numels(w.tensors), w.world, w.bucket_cap)
+    if w.plan_layout == "dim0":
+        pl = OP.make_plan_dim0([s for _n, s in w.tensors], w.world)
+    else:
+        pl = OP.make_plan(W.numels(w.tensors), w.world, w.bucket_cap)
     segs = OP.rank_segments(pl, w.rank)
     return pl, W.Layout(S=pl.shard_numel, segments=segs, tensor_flat_off=list(pl.tensor_offset))
+
+
+def device_plan(w: W.Workload) -> Z.Plan:
+    if w.plan_layout == "dim0":
+        return Z.Plan.dim0([s for _n, s in w.tensors], w.world)
+    return Z.Plan(W.numels(w.tensors), w.world, w.bucket_cap)
 
 
 def round_up(x: int, m: int) -> int:
@@ -124,7 +133,7 @@ class Rig:
         self.w = w
         self.pl, self.lay = oracle_layout(w)
         self.S = self.lay.S
-        self.plan = Z.Plan(W.numels(w.tensors), w.world, w.bucket_cap)
+        self.plan = device_plan(w)
         self.ld = round_up(self.S, ld_align)
         dev = torch.device(device)
         self.dev = dev

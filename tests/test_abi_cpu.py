@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared_functions():
     src = open(os.path.join(ROOT, "include", "zero_shard.h"), encoding="utf-8").read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"\b(zero_[a-z_]+)\s*\(", src)
+    names = re.findall(r"\b(zero_[a-z0-9_]+)\s*\(", src)
     return sorted(set(names))
 
 
@@ -58,6 +58,43 @@ def test_planner_matches_oracle(sizes, world, cap):
         assert pb == OP.padded_model_state_bytes(o, stage)
         exact = OP.model_state_bytes(sum(sizes), world, stage)
         assert abs(f - float(exact)) <= 1e-12 * float(exact)
+
+
+DIM0_CASES = [
+    ([(256, 64), (256,), (10, 256), (10,)], 2),
+    ([(256, 64), (256,), (10, 256), (10,)], 3),
+    ([(0, 5), (3, 2), (0,), (4,), (), (7, 0), (1, 1, 9)], 4),
+    ([(5,)], 8),
+    ([(50257, 1600), (1024, 1600), (1600,), (1600, 4800), (4800,)], 8),
+    ([tuple(s) for _n, s in W.gpt2(n_layer=2)], 64),
+]
+
+
+@pytest.mark.parametrize("shapes,world", DIM0_CASES)
+def test_dim0_planner_matches_oracle(shapes, world):
+    o = OP.make_plan_dim0(shapes, world)
+    p = Z.Plan.dim0(shapes, world)
+    assert (p.shard_numel, p.total_numel, p.padded_numel) == (o.shard_numel, o.psi, o.padded_numel)
+    assert p.num_buckets == len(o.buckets) and p.num_tensors == len(shapes)
+    for b, ob in enumerate(o.buckets):
+        assert p.bucket(b) == (ob.base, ob.numel, ob.padded, ob.shard, ob.first_tensor, ob.n_tensors)
+    for i in range(len(shapes)):
+        assert p.tensor(i) == (o.tensor_bucket[i], o.tensor_offset[i])
+    for r in (range(world) if world <= 8 else [0, 1, world - 1]):
+        assert p.segments(r) == OP.rank_segments(o, r)
+
+
+@pytest.mark.parametrize("bad", [dict(rows=[], rn=[], world=2), dict(rows=[0, 3], rn=[4, 0], world=2),
+                                 dict(rows=[4], rn=[1], world=0), dict(rows=[-1], rn=[5], world=2),
+                                 dict(rows=[1 << 40], rn=[1 << 20], world=2)])
+def test_dim0_plan_rejects(bad):
+    import ctypes as C
+    n = len(bad["rows"])
+    h = C.c_void_p()
+    rc = Z.lib().zero_plan_dim0((C.c_int64 * max(n, 1))(*bad["rows"]), (C.c_int64 * max(n, 1))(*bad["rn"]),
+                                n, bad["world"], C.byref(h))
+    assert rc == Z.ZERO_EINVAL and not h.value
+    assert "zero_plan_dim0" in Z.zero_last_error()
 
 
 @pytest.mark.parametrize("bad", [dict(numels=[], world=2), dict(numels=[0, 0], world=2),

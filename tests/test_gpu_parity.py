@@ -379,3 +379,38 @@ def test_full_gradient_overflow_only_in_own_pieces(inside):
     gref = rig.gather0.copy()
     OS.write_gather(gref, segs, res.params)
     assert np.array_equal(rig.gather_np(), gref)
+
+
+# ---------------------------------------------------------------------------
+# per-parameter dim-0 layout (FSDP2 fully_shard): one piece per parameter
+# ---------------------------------------------------------------------------
+
+def _dim0(tensors, world, rank, g, p, **kw):
+    kw.setdefault("weight_decay", 0.05)
+    return W.Workload(name=f"dim0_{len(tensors)}t_n{world}_r{rank}_{g}_{p}", tensors=tuple(tensors),
+                      world=world, rank=rank, bucket_cap=0, grad_dtype=g, param_dtype=p, lr=1e-3,
+                      steps=2, seed=11, plan_layout="dim0", **kw)
+
+
+@pytest.mark.parametrize("rank", [0, 1])
+def test_dim0_page_mlp(rank):
+    """The handbook's FSDP2 example model on 2 ranks (weights (256, 64), (10, 256))."""
+    tm = [("0.weight", (256, 64)), ("0.bias", (256,)), ("2.weight", (10, 256)), ("2.bias", (10,))]
+    run_workload(_dim0(tm, 2, rank, "f32", "f32"), layout=TILED)
+    run_workload(_dim0(tm, 2, rank, "bf16", "bf16"))
+
+
+@pytest.mark.parametrize("source", ["slices", "stored", "full"])
+@pytest.mark.parametrize("g,p", [("bf16", "bf16"), ("f16", "f16"), ("f32", "f32")])
+@pytest.mark.parametrize("world,rank,n_layer", [(8, 7, 2), (8, 3, 4), (16, 0, 1)])
+def test_dim0_gpt2_shapes(world, rank, n_layer, g, p, source):
+    """GPT-2-shaped parameter lists (d = 64): 28 to 52 pieces, several launch
+    groups, pieces of every size down to a few elements."""
+    ts = W.gpt2(n_layer=n_layer, d=64, vocab=503, n_ctx=96)
+    ls = 256.0 if g == "f16" else 1.0
+    run_workload(_dim0(ts, world, rank, g, p, loss_scale=ls), layout=TILED, source=source)
+
+
+def test_dim0_clipped():
+    ts = W.gpt2(n_layer=3, d=64, vocab=503, n_ctx=96)
+    run_workload(_dim0(ts, 8, 5, "bf16", "bf16", max_norm=0.02), layout=TILED)

@@ -89,7 +89,7 @@ class Workload:
     tensors: Tuple[Tensor, ...]
     world: int                     # N, data-parallel degree
     rank: int                      # the rank whose shard is stepped
-    bucket_cap: int                # <= 0: one flat bucket
+    bucket_cap: int                # <= 0: one flat bucket (ignored by the dim0 layout)
     grad_dtype: str                # "f32" | "bf16" | "f16": dtype of the N slices
     param_dtype: str               # "f32" | "bf16" | "f16": dtype written to the gather slot
     lr: float
@@ -109,6 +109,7 @@ class Workload:
     v_sigma: float = 0.0           # 0: v starts at 0; else v = |N(0, v_sigma)|
     inject_inf_step: Optional[int] = None  # 1-based step whose slices carry one +inf
     seed: int = 0
+    plan_layout: str = "flat"      # "flat": flat buckets; "dim0": per-parameter dim-0 split
 
     @property
     def psi(self) -> int:

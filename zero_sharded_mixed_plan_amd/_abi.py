@@ -24,7 +24,7 @@ DTYPE_BYTES = {ZERO_F32: 4, ZERO_BF16: 2, ZERO_F16: 2}
 
 # every symbol the header declares
 EXPORTS = [
-    "zero_plan", "zero_plan_free", "zero_plan_shard_numel", "zero_plan_total_numel",
+    "zero_plan", "zero_plan_dim0", "zero_plan_free", "zero_plan_shard_numel", "zero_plan_total_numel",
     "zero_plan_padded_numel", "zero_plan_world", "zero_plan_num_buckets", "zero_plan_num_tensors",
     "zero_plan_bucket", "zero_plan_tensor", "zero_plan_rank_segment", "zero_plan_bytes",
     "zero_state_numel", "zero_workspace_bytes", "zero_reduce_shard", "zero_shard_norm", "zero_adam_step",
@@ -82,8 +82,9 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def load(path: str) -> ctypes.CDLL:
-    """Load one build of the library from `path` and declare its C signatures."""
+def load(path: str, required: bool = True) -> ctypes.CDLL:
+    """Load one build of the library from `path` and declare its C signatures
+    (required=False skips entry points an older build does not export)."""
     # torch first: the library must bind to the HIP runtime torch already uses
     # for the device memory and streams it hands over (one runtime per process)
     import torch  # noqa: F401
@@ -95,6 +96,7 @@ def load(path: str) -> ctypes.CDLL:
     P64, P32 = ctypes.POINTER(i64), ctypes.POINTER(i32)
     sig = {
         "zero_plan": (ctypes.c_int, [P64, i32, i32, i64, ctypes.POINTER(vp)]),
+        "zero_plan_dim0": (ctypes.c_int, [P64, P64, i32, i32, ctypes.POINTER(vp)]),
         "zero_plan_free": (None, [vp]),
         "zero_plan_shard_numel": (i64, [vp]),
         "zero_plan_total_numel": (i64, [vp]),
@@ -115,6 +117,8 @@ def load(path: str) -> ctypes.CDLL:
         "zero_version": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
+        if not required and not hasattr(L, name):
+            continue
         fn = getattr(L, name)
         fn.restype = res
         fn.argtypes = args
@@ -141,13 +145,32 @@ def zero_version() -> str:
 class Plan:
     """Owner of a zero_plan_t handle."""
 
-    def __init__(self, numels, world: int, bucket_cap: int = 0):
+    def __init__(self, numels, world: int, bucket_cap: int = 0, *, _handle=None):
         L = lib()
-        arr = (ctypes.c_int64 * len(numels))(*[int(n) for n in numels])
-        h = ctypes.c_void_p()
-        _check(L.zero_plan(arr, len(numels), int(world), int(bucket_cap), ctypes.byref(h)))
-        self._h = h
+        if _handle is None:
+            arr = (ctypes.c_int64 * len(numels))(*[int(n) for n in numels])
+            h = ctypes.c_void_p()
+            _check(L.zero_plan(arr, len(numels), int(world), int(bucket_cap), ctypes.byref(h)))
+            _handle = h
+        self._h = _handle
         self.world = int(world)
+
+    @classmethod
+    def dim0(cls, shapes, world: int) -> "Plan":
+        """Per-parameter dim-0 layout (zero_plan_dim0) of parameters of the given shapes."""
+        rows, row_numel = [], []
+        for sh in shapes:
+            sh = tuple(int(x) for x in sh)
+            rows.append(sh[0] if sh else 1)
+            k = 1
+            for x in sh[1:]:
+                k *= x
+            row_numel.append(k)
+        n = len(rows)
+        h = ctypes.c_void_p()
+        _check(lib().zero_plan_dim0((ctypes.c_int64 * n)(*rows), (ctypes.c_int64 * n)(*row_numel), n,
+                                    int(world), ctypes.byref(h)))
+        return cls(None, world, _handle=h)
 
     @property
     def handle(self) -> ctypes.c_void_p:

@@ -324,10 +324,48 @@ __device__ __forceinline__ int64_t state_off(const StepLaunch& a, int64_t j) {
   return (j >> a.st_shift) * a.st_stride + (j & a.st_mask);
 }
 
-// gather index offset of local element j (uniform loop over the launch's pieces)
-__device__ __forceinline__ int64_t delta_of(const StepLaunch& a, int64_t j) {
-  int64_t d = a.seg[0].delta;
-  for (int s = 0; s + 1 < a.nseg; ++s)
+// The value of x in the wave's first active lane: tells the compiler that a
+// quantity computed the same way in every lane is uniform (scalar registers).
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The launch's pieces that can hold a wave's local elements [lo, hi): a
+// uniform binary search over the piece ends (increasing), so a lane's lookup
+// below scans only the few pieces the wave touches, not all of them.
+struct SegRange {
+  int s0, s1;  // pieces s0 .. s1
+};
+
+__device__ __forceinline__ SegRange wave_segs(const StepLaunch& a, int64_t lo, int64_t hi) {
+  // a few pieces: scan them all (no chain of dependent argument loads)
+  if (a.nseg <= kScanSeg) return SegRange{0, a.nseg - 1};
+  int L = 0, R = a.nseg - 1;
+  while (L < R) {  // first piece ending after lo
+    const int M = (L + R) >> 1;
+    if (a.seg[M].end > lo) R = M; else L = M + 1;
+  }
+  const int s0 = L;
+  R = a.nseg - 1;
+  while (L < R) {  // first piece reaching hi
+    const int M = (L + R) >> 1;
+    if (a.seg[M].end >= hi) R = M; else L = M + 1;
+  }
+  return SegRange{s0, L};
+}
+
+// the wave's pieces, from its first vector index (any lane's v minus its lane)
+__device__ __forceinline__ SegRange wave_segs_v(const StepLaunch& a, int64_t v) {
+  const int64_t w0 = uniform64(v - (int64_t)(threadIdx.x & 63));
+  return wave_segs(a, w0 * kVec, (w0 + 64) * kVec);
+}
+
+// gather index offset of local element j, j inside the wave's pieces
+__device__ __forceinline__ int64_t delta_of(const StepLaunch& a, const SegRange& r, int64_t j) {
+  int64_t d = a.seg[r.s0].delta;
+  for (int s = r.s0; s < r.s1; ++s)
     if (j >= a.seg[s].end) d = a.seg[s + 1].delta;
   return d;
 }
@@ -338,23 +376,24 @@ __device__ __forceinline__ int64_t delta_of(const StepLaunch& a, int64_t j) {
 // by element (a piece boundary inside the 8, or a slot that is not 16-byte
 // aligned).
 template <class GT, int NB>
-__device__ __forceinline__ void reduce8_pieces(const StepLaunch& a, int64_t j0, float acc[8]) {
+__device__ __forceinline__ void reduce8_pieces(const StepLaunch& a, const SegRange& sr, int64_t j0,
+                                               float acc[8]) {
   const char* g = static_cast<const char*>(a.grad);
-  const int64_t d0 = delta_of(a, j0);
+  const int64_t d0 = delta_of(a, sr, j0);
   const char* p = g + (j0 + d0) * GT::bytes;
-  if (delta_of(a, j0 + kVec - 1) == d0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+  if (delta_of(a, sr, j0 + kVec - 1) == d0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
     reduce8<GT, NB>(p, a.ld_bytes, a.n, acc);
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      acc[e] = reduce1<GT>(g + (j0 + e + delta_of(a, j0 + e)) * GT::bytes, a.ld_bytes, a.n);
+      acc[e] = reduce1<GT>(g + (j0 + e + delta_of(a, sr, j0 + e)) * GT::bytes, a.ld_bytes, a.n);
   }
 }
 
 // the gradient of local element j in slice 0
 template <class GT>
-__device__ __forceinline__ const char* grad_elem(const StepLaunch& a, int64_t j) {
-  return static_cast<const char*>(a.grad) + (j + (a.grad_full ? delta_of(a, j) : 0)) * GT::bytes;
+__device__ __forceinline__ const char* grad_elem(const StepLaunch& a, const SegRange& sr, int64_t j) {
+  return static_cast<const char*>(a.grad) + (j + (a.grad_full ? delta_of(a, sr, j) : 0)) * GT::bytes;
 }
 
 // ---------------------------------------------------------------------------
@@ -372,6 +411,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
   const int64_t v = a.v_lo + (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (v >= a.v_hi) return;
   const int64_t j0 = v * kVec;
+  const SegRange sr = wave_segs_v(a, v);
   float clip = 1.0f;
   if (STASH && a.clip != nullptr) clip = *a.clip;
 
@@ -401,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
                                       load_state);
       } else {
         load_state();
-        if (a.grad_full) reduce8_pieces<GT, NB>(a, j0, acc);
+        if (a.grad_full) reduce8_pieces<GT, NB>(a, sr, j0, acc);
         else reduce8<GT, NB>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes, a.n, acc);
       }
 #pragma unroll
@@ -415,12 +455,12 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
     st8(a.p_out + o0, p);
     st8(a.m_out + o0, m);
     st8(a.v_out + o0, s);
-    const int64_t d0 = delta_of(a, j0);
-    if (delta_of(a, j0 + kVec - 1) == d0) {
+    const int64_t d0 = delta_of(a, sr, j0);
+    if (delta_of(a, sr, j0 + kVec - 1) == d0) {
       store_params8<PT>(a.gather + (j0 + d0) * PT::bytes, p);
     } else {  // the 8 elements straddle two gather pieces
 #pragma unroll
-      for (int e = 0; e < 8; ++e) store_param1<PT>(a.gather + (j0 + e + delta_of(a, j0 + e)) * PT::bytes, p[e]);
+      for (int e = 0; e < 8; ++e) store_param1<PT>(a.gather + (j0 + e + delta_of(a, sr, j0 + e)) * PT::bytes, p[e]);
     }
   } else {
     // the shard's ragged end: fewer than 8 elements, element by element
@@ -432,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
       if (STASH) {
         ge = a.g_stash[j] * clip;
       } else {
-        const float acc = reduce1<GT>(grad_elem<GT>(a, j), a.ld_bytes, a.n);
+        const float acc = reduce1<GT>(grad_elem<GT>(a, sr, j), a.ld_bytes, a.n);
         ge = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, a.inv_scale);
         bad |= !__builtin_isfinite(ge);
       }
@@ -440,7 +480,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
       a.p_out[oj] = pe;
       a.m_out[oj] = me;
       a.v_out[oj] = ve;
-      store_param1<PT>(a.gather + (j + delta_of(a, j)) * PT::bytes, pe);
+      store_param1<PT>(a.gather + (j + delta_of(a, sr, j)) * PT::bytes, pe);
     }
   }
   if (!STASH && a.overflow != nullptr && bad) atomicOr(a.overflow, 1u);
@@ -460,6 +500,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
     return;
   }
   const int64_t j0 = (int64_t)threadIdx.x * kVec;
+  const SegRange sr = wave_segs_v(a, threadIdx.x);
   const int64_t rest = a.S - j0;
   const int cnt = rest >= kVec ? kVec : (rest > 0 ? (int)rest : 0);
   float g[8];
@@ -467,7 +508,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
   if (cnt == kVec) {
     float acc[8];
     if (a.grad_full)
-      reduce8_pieces<GT, Batch<GT, false>::value>(a, j0, acc);
+      reduce8_pieces<GT, Batch<GT, false>::value>(a, sr, j0, acc);
     else
       reduce8<GT, Batch<GT, false>::value>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes,
                                            a.n, acc);
@@ -477,7 +518,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
     for (int e = 0; e < 8; ++e) {
       g[e] = 0.0f;
       if (e < cnt) {
-        const float acc = reduce1<GT>(grad_elem<GT>(a, j0 + e), a.ld_bytes, a.n);
+        const float acc = reduce1<GT>(grad_elem<GT>(a, sr, j0 + e), a.ld_bytes, a.n);
         g[e] = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, a.inv_scale);
       }
     }
@@ -498,11 +539,11 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
     st8(a.p_out + o0, p);
     st8(a.m_out + o0, m);
     st8(a.v_out + o0, v);
-    const int64_t d0 = delta_of(a, j0);
-    if (delta_of(a, j0 + kVec - 1) == d0) {
+    const int64_t d0 = delta_of(a, sr, j0);
+    if (delta_of(a, sr, j0 + kVec - 1) == d0) {
       store_params8<PT>(a.gather + (j0 + d0) * PT::bytes, p);
     } else {
-      for (int e = 0; e < 8; ++e) store_param1<PT>(a.gather + (j0 + e + delta_of(a, j0 + e)) * PT::bytes, p[e]);
+      for (int e = 0; e < 8; ++e) store_param1<PT>(a.gather + (j0 + e + delta_of(a, sr, j0 + e)) * PT::bytes, p[e]);
     }
   } else {
     for (int e = 0; e < cnt; ++e) {
@@ -513,7 +554,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
       a.p_out[oj] = pe;
       a.m_out[oj] = me;
       a.v_out[oj] = ve;
-      store_param1<PT>(a.gather + (j + delta_of(a, j)) * PT::bytes, pe);
+      store_param1<PT>(a.gather + (j + delta_of(a, sr, j)) * PT::bytes, pe);
     }
   }
 }
@@ -526,18 +567,19 @@ __global__ __launch_bounds__(kThreads) void recast_kernel(const StepLaunch a, co
   for (int64_t v = a.v_lo + (int64_t)blockIdx.x * kThreads + threadIdx.x; v < a.v_hi;
        v += (int64_t)gridDim.x * kThreads) {
     const int64_t j0 = v * kVec;
+    const SegRange sr = wave_segs_v(a, v);
     if (j0 + kVec <= a.S) {
       float p[8];
       ld8(a.p_in + state_off(a, j0), p);
-      const int64_t d0 = delta_of(a, j0);
-      if (delta_of(a, j0 + kVec - 1) == d0) {
+      const int64_t d0 = delta_of(a, sr, j0);
+      if (delta_of(a, sr, j0 + kVec - 1) == d0) {
         store_params8<PT>(a.gather + (j0 + d0) * PT::bytes, p);
       } else {
-        for (int e = 0; e < 8; ++e) store_param1<PT>(a.gather + (j0 + e + delta_of(a, j0 + e)) * PT::bytes, p[e]);
+        for (int e = 0; e < 8; ++e) store_param1<PT>(a.gather + (j0 + e + delta_of(a, sr, j0 + e)) * PT::bytes, p[e]);
       }
     } else {
       for (int64_t j = j0; j < a.S; ++j)
-        store_param1<PT>(a.gather + (j + delta_of(a, j)) * PT::bytes, a.p_in[state_off(a, j)]);
+        store_param1<PT>(a.gather + (j + delta_of(a, sr, j)) * PT::bytes, a.p_in[state_off(a, j)]);
     }
   }
 }

@@ -77,6 +77,68 @@ extern "C" int zero_plan(const int64_t* numel, int32_t n_tensors, int32_t world,
   return ZERO_OK;
 }
 
+// Per-parameter dim-0 layout ("ZeRO 与 FSDP…", section "ZeRO-3 与 FSDP": fully_shard
+// splits each parameter on its first dimension).  One bucket per non-empty
+// parameter with its rows padded to a multiple of N; empty parameters ride
+// along in a neighbouring bucket without adding to it.
+extern "C" int zero_plan_dim0(const int64_t* rows, const int64_t* row_numel, int32_t n_tensors,
+                              int32_t world, zero_plan_t** out) {
+  if (!out) return fail(ZERO_EINVAL, "zero_plan_dim0: out is NULL");
+  *out = nullptr;
+  if (!rows || !row_numel || n_tensors <= 0) return fail(ZERO_EINVAL, "zero_plan_dim0: need at least one tensor");
+  if (world < 1) return fail(ZERO_EINVAL, "zero_plan_dim0: world must be >= 1");
+  const int64_t kMax = int64_t(1) << 52;
+  int64_t psi = 0;
+  for (int32_t i = 0; i < n_tensors; ++i) {
+    if (rows[i] < 0 || row_numel[i] < 0) return fail(ZERO_EINVAL, "zero_plan_dim0: negative size");
+    if (rows[i] > kMax || row_numel[i] > kMax || (row_numel[i] > 0 && rows[i] > kMax / row_numel[i]))
+      return fail(ZERO_EINVAL, "zero_plan_dim0: sizes too large");
+    psi += rows[i] * row_numel[i];
+    if (psi > kMax) return fail(ZERO_EINVAL, "zero_plan_dim0: sizes too large");
+  }
+  if (psi == 0) return fail(ZERO_EINVAL, "zero_plan_dim0: all tensors are empty");
+
+  zero_plan_t* p = new (std::nothrow) zero_plan_t;
+  if (!p) return fail(ZERO_ENOMEM, "zero_plan_dim0: out of host memory");
+  try {
+    p->world = world;
+    p->psi = psi;
+    p->numel.resize(n_tensors);
+    for (int32_t i = 0; i < n_tensors; ++i) p->numel[i] = rows[i] * row_numel[i];
+    p->tensor_bucket.resize(n_tensors);
+    p->tensor_offset.resize(n_tensors);
+    // groups [first, end) each holding exactly one non-empty parameter
+    int32_t first = 0;
+    while (first < n_tensors) {
+      int32_t main = first;
+      while (p->numel[main] == 0) ++main;  // a non-empty one exists at or after `first`
+      int32_t end = main + 1;
+      while (end < n_tensors && p->numel[end] == 0) ++end;
+      zero_plan_t::Bucket b;
+      b.first = first;
+      b.count = end - first;
+      b.numel = p->numel[main];
+      b.shard = (rows[main] + world - 1) / world * row_numel[main];
+      b.padded = b.shard * world;
+      b.base = p->padded;
+      b.local_off = p->shard;
+      for (int32_t i = first; i < end; ++i) {
+        p->tensor_bucket[i] = (int32_t)p->buckets.size();
+        p->tensor_offset[i] = b.base + (i > main ? b.numel : 0);
+      }
+      p->buckets.push_back(b);
+      p->padded += b.padded;
+      p->shard += b.shard;
+      first = end;
+    }
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(ZERO_ENOMEM, "zero_plan_dim0: out of host memory");
+  }
+  *out = p;
+  return ZERO_OK;
+}
+
 extern "C" void zero_plan_free(zero_plan_t* plan) { delete plan; }
 
 extern "C" int64_t zero_plan_shard_numel(const zero_plan_t* p) { return p ? p->shard : -1; }

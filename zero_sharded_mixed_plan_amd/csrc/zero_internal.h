@@ -31,7 +31,8 @@ int fail(int code, const std::string& msg);
 constexpr int kThreads = 256;   // threads per workgroup (4 wave64s)
 constexpr int kVec = 8;         // elements per thread per tile
 constexpr int kTile = kThreads * kVec;
-constexpr int kMaxSeg = 24;     // gather pieces one launch of the update kernel can address
+constexpr int kMaxSeg = 192;    // gather pieces one launch of the update kernel can address
+constexpr int kScanSeg = 24;    // up to this many pieces, a lane scans all of them
 constexpr int kNormThreads = 256;     // threads of the norm finalize workgroups
 constexpr int kNormGroups = 256;      // first-level workgroups of the norm finalize
 constexpr int kStateTileShift = 11;   // tiled state: 2048 elements of master, m, v per tile
@@ -85,6 +86,9 @@ struct StepLaunch {
   int32_t nseg;
   Seg seg[kMaxSeg];
 };
+
+// passed by value as the kernel argument: within the 4 KiB kernel-argument limit
+static_assert(sizeof(StepLaunch) <= 3584, "StepLaunch must fit the kernel-argument segment");
 
 struct ReduceLaunch {
   const void* grad;
