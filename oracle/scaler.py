@@ -39,5 +39,7 @@ def update(s: ScalerState, overflow: bool) -> ScalerState:
 
 
 def inv_scale(s: ScalerState) -> np.float32:
-    """fp32(1 / scale): what the step multiplies the averaged gradient by."""
-    return F32(1.0 / float(s.scale))
+    """fp32(1 / scale): what the step multiplies the averaged gradient by (IEEE
+    division: a scale that has underflowed to 0 gives +inf)."""
+    with np.errstate(divide="ignore", over="ignore"):
+        return F32(np.float64(1.0) / np.float64(s.scale))

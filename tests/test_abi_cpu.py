@@ -223,18 +223,21 @@ def test_tiled_state_validation(over, code):
     assert e.value.code == code, Z.zero_last_error()
 
 
-def test_args_struct_layout_matches_header(tmp_path):
-    """The ctypes mirror of zero_adam_args_t has the header's field offsets and
-    size (compiled with the host C compiler against include/zero_shard.h)."""
+@pytest.mark.parametrize("cname,pytype", [("zero_adam_args_t", Z.zero_adam_args_t),
+                                           ("zero_scaler_t", Z.zero_scaler_t),
+                                           ("zero_ckpt_meta_t", Z.zero_ckpt_meta_t)])
+def test_args_struct_layout_matches_header(cname, pytype, tmp_path):
+    """The ctypes mirrors of the ABI structs have the header's field offsets
+    and sizes (compiled with the host C compiler against include/zero_shard.h)."""
     import shutil
     import subprocess
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no host C compiler")
-    fields = [f for f, _ in Z.zero_adam_args_t._fields_]
+    fields = [f for f, _ in pytype._fields_]
     prog = ["#include <stdio.h>", "#include <stddef.h>", '#include "zero_shard.h"', "int main(void) {",
-            '  printf("%zu\\n", sizeof(zero_adam_args_t));']
-    prog += [f'  printf("%zu\\n", offsetof(zero_adam_args_t, {f}));' for f in fields]
+            f'  printf("%zu\\n", sizeof({cname}));']
+    prog += [f'  printf("%zu\\n", offsetof({cname}, {f}));' for f in fields]
     prog += ["  return 0;", "}"]
     src = tmp_path / "layout.c"
     src.write_text("\n".join(prog) + "\n")
@@ -243,6 +246,6 @@ def test_args_struct_layout_matches_header(tmp_path):
                    check=True)
     out = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
                                           text=True).stdout.split()]
-    assert out[0] == ctypes.sizeof(Z.zero_adam_args_t)
+    assert out[0] == ctypes.sizeof(pytype)
     for f, off in zip(fields, out[1:]):
-        assert getattr(Z.zero_adam_args_t, f).offset == off, f
+        assert getattr(pytype, f).offset == off, f

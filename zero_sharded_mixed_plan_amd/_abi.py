@@ -14,7 +14,7 @@ from typing import List, Tuple
 LIB_PATH = os.environ.get("ZERO_SHARD_LIB") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libzero_shard.so")
 
-ZERO_OK, ZERO_EINVAL, ZERO_EALIGN, ZERO_ENOMEM, ZERO_EHIP = 0, -1, -2, -3, -4
+ZERO_OK, ZERO_EINVAL, ZERO_EALIGN, ZERO_ENOMEM, ZERO_EHIP, ZERO_EIO = 0, -1, -2, -3, -4, -5
 ZERO_F32, ZERO_BF16, ZERO_F16 = 0, 1, 2
 ZERO_STATE_SEPARATE, ZERO_STATE_TILED = 0, 1
 ZERO_STATE_TILE = 2048
@@ -28,7 +28,8 @@ EXPORTS = [
     "zero_plan_padded_numel", "zero_plan_world", "zero_plan_num_buckets", "zero_plan_num_tensors",
     "zero_plan_bucket", "zero_plan_tensor", "zero_plan_rank_segment", "zero_plan_bytes",
     "zero_state_numel", "zero_workspace_bytes", "zero_reduce_shard", "zero_shard_norm", "zero_adam_step",
-    "zero_last_error", "zero_version",
+    "zero_scaler_init", "zero_scaler_update", "zero_scaler_inv_scale", "zero_plan_hash",
+    "zero_checkpoint_save", "zero_checkpoint_load", "zero_last_error", "zero_version",
 ]
 
 
@@ -69,6 +70,20 @@ class zero_adam_args_t(ctypes.Structure):
         ("ev_begin", ctypes.c_void_p),
         ("ev_end", ctypes.c_void_p),
     ]
+
+
+class zero_scaler_t(ctypes.Structure):
+    _fields_ = [
+        ("scale", ctypes.c_float),
+        ("growth_tracker", ctypes.c_int32),
+        ("growth_factor", ctypes.c_float),
+        ("backoff_factor", ctypes.c_float),
+        ("growth_interval", ctypes.c_int32),
+    ]
+
+
+class zero_ckpt_meta_t(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int64), ("scaler", zero_scaler_t)]
 
 
 _lib = None
@@ -113,6 +128,14 @@ def load(path: str, required: bool = True) -> ctypes.CDLL:
         "zero_reduce_shard": (ctypes.c_int, [vp, vp, i64, i32, ctypes.c_int, f32, vp, vp, i32, vp]),
         "zero_shard_norm": (ctypes.c_int, [vp, vp, f64, f64, vp, vp, vp, vp]),
         "zero_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(zero_adam_args_t), vp]),
+        "zero_scaler_init": (ctypes.c_int, [ctypes.POINTER(zero_scaler_t), f32, f32, f32, i32]),
+        "zero_scaler_update": (ctypes.c_int, [ctypes.POINTER(zero_scaler_t), i32]),
+        "zero_scaler_inv_scale": (f32, [ctypes.POINTER(zero_scaler_t)]),
+        "zero_plan_hash": (ctypes.c_uint64, [vp]),
+        "zero_checkpoint_save": (ctypes.c_int, [vp, i32, ctypes.c_char_p, i32, vp, vp, vp,
+                                                ctypes.POINTER(zero_ckpt_meta_t), vp]),
+        "zero_checkpoint_load": (ctypes.c_int, [vp, i32, ctypes.c_char_p, i32, vp, vp, vp,
+                                                ctypes.POINTER(zero_ckpt_meta_t), vp]),
         "zero_last_error": (ctypes.c_char_p, []),
         "zero_version": (ctypes.c_char_p, []),
     }
@@ -274,6 +297,58 @@ def zero_shard_norm(plan: Plan, ws: int, other_ranks_sumsq: float, max_norm: flo
 
 def zero_adam_step(plan: Plan, args: zero_adam_args_t, stream: int = 0) -> None:
     _check(lib().zero_adam_step(plan.handle, ctypes.byref(args), stream or None))
+
+
+# ---------------------------------------------------------------------------
+# loss scale and sharded checkpoints (host)
+# ---------------------------------------------------------------------------
+
+class Scaler:
+    """Dynamic loss scale (zero_scaler_t): update() after every step with its
+    overflow flag; inv_scale is what the step multiplies the gradient by."""
+
+    def __init__(self, init_scale: float = 65536.0, growth_factor: float = 2.0,
+                 backoff_factor: float = 0.5, growth_interval: int = 2000):
+        self.s = zero_scaler_t()
+        _check(lib().zero_scaler_init(ctypes.byref(self.s), init_scale, growth_factor, backoff_factor,
+                                      int(growth_interval)))
+
+    def update(self, overflow: bool) -> None:
+        _check(lib().zero_scaler_update(ctypes.byref(self.s), 1 if overflow else 0))
+
+    @property
+    def scale(self) -> float:
+        return self.s.scale
+
+    @property
+    def growth_tracker(self) -> int:
+        return self.s.growth_tracker
+
+    @property
+    def inv_scale(self) -> float:
+        return lib().zero_scaler_inv_scale(ctypes.byref(self.s))
+
+
+def zero_plan_hash(plan: Plan) -> int:
+    return lib().zero_plan_hash(plan.handle)
+
+
+def zero_checkpoint_save(plan: Plan, rank: int, path: str, state_layout: int, master: int, m: int, v: int,
+                         step: int, scaler: zero_scaler_t, stream: int = 0) -> None:
+    meta = zero_ckpt_meta_t(step=int(step), scaler=scaler)
+    _check(lib().zero_checkpoint_save(plan.handle, int(rank), os.fsencode(path), int(state_layout),
+                                      master or None, m or None, v or None, ctypes.byref(meta),
+                                      stream or None))
+
+
+def zero_checkpoint_load(plan: Plan, rank: int, path: str, state_layout: int, master: int, m: int, v: int,
+                         stream: int = 0) -> zero_ckpt_meta_t:
+    """Returns the saved metadata (step and scaler)."""
+    meta = zero_ckpt_meta_t()
+    _check(lib().zero_checkpoint_load(plan.handle, int(rank), os.fsencode(path), int(state_layout),
+                                      master or None, m or None, v or None, ctypes.byref(meta),
+                                      stream or None))
+    return meta
 
 
 def adam_args(**kw) -> zero_adam_args_t:

@@ -68,30 +68,38 @@ def state_arg_dict(layout: int, src, dst) -> dict:
 class ZeroAdam:
     """Sharded AdamW state and step of rank `rank` out of `world`.
 
-    Without clipping the step is one fused pass over the N slices and writes the
-    new state into the second of two state buffers, which become current only
-    if no gradient overflowed.  With max_norm > 0 the step is two passes: the
-    reduced gradient and the norm partials first, then the update in place.
-    Loss-scale policy (the pages show only GradScaler's API): the scale halves on
-    an overflow and doubles after `growth_interval` clean steps.
+    Without clipping the step is one fused pass over the gradient buffers and
+    writes the new state into the second of two state buffers, which become
+    current only if no gradient overflowed.  With max_norm > 0 the step is two
+    passes: the reduced gradient and the norm partials first, then the update
+    in place.  With dynamic_loss_scale the loss scale follows zero_scaler_t
+    (backoff on an overflow, growth after `growth_interval` clean steps).
+
+    layout "flat": `numels` are tensor sizes packed into flat buckets of
+    `bucket_cap`; layout "dim0": `numels` are parameter shapes, each split on
+    its first dimension (FSDP2 fully_shard).
     """
 
-    def __init__(self, numels: Sequence[int], world: int, rank: int, *, lr: float,
+    def __init__(self, numels: Sequence, world: int, rank: int, *, lr: float,
                  betas=(0.9, 0.999), eps: float = 1e-8, weight_decay: float = 0.0,
                  bucket_cap: int = 0, grad_dtype=torch.bfloat16, param_dtype=torch.bfloat16,
                  max_norm: float = 0.0, loss_scale: float = 1.0, dynamic_loss_scale: bool = False,
                  growth_interval: int = 2000, master: Optional[torch.Tensor] = None,
                  gather: Optional[torch.Tensor] = None, device="cuda",
-                 state_layout: int = _abi.ZERO_STATE_TILED):
-        self.plan = _abi.Plan(numels, world, bucket_cap)
+                 state_layout: int = _abi.ZERO_STATE_TILED, layout: str = "flat"):
+        if layout == "dim0":
+            self.plan = _abi.Plan.dim0(numels, world)
+        elif layout == "flat":
+            self.plan = _abi.Plan(numels, world, bucket_cap)
+        else:
+            raise ValueError("layout must be 'flat' or 'dim0'")
         self.world, self.rank = int(world), int(rank)
         self.lr, self.betas, self.eps, self.weight_decay = lr, tuple(betas), eps, weight_decay
         self.grad_dtype, self.param_dtype = grad_dtype, param_dtype
         self.max_norm = float(max_norm)
-        self.loss_scale = float(loss_scale)
         self.dynamic = dynamic_loss_scale
-        self.growth_interval = growth_interval
-        self._clean = 0
+        # a fixed scale is a scaler that is never updated
+        self.scaler = _abi.Scaler(float(loss_scale), 2.0, 0.5, growth_interval)
         self.t = 0
         self.skipped = 0
         S = self.plan.shard_numel
@@ -123,6 +131,10 @@ class ZeroAdam:
             self.sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
             self.clip = torch.ones(1, **f32)
 
+    @property
+    def loss_scale(self) -> float:
+        return self.scaler.scale
+
     # -- state ---------------------------------------------------------------
     def state(self):
         """(master, m, v) of this rank as [S] tensors (copies for the tiled layout)."""
@@ -150,23 +162,52 @@ class ZeroAdam:
     def segments(self):
         return self.plan.segments(self.rank)
 
+    # -- sharded checkpoint ----------------------------------------------------
+    def _ptrs(self):
+        cur = self._state[self._cur]
+        if self.layout == _abi.ZERO_STATE_TILED:
+            return cur[0].data_ptr(), 0, 0
+        return tuple(x.data_ptr() for x in cur)
+
+    def save(self, path: str) -> None:
+        """Write this rank's shard (master, m, v, t, loss-scale state) to `path`."""
+        _abi.zero_checkpoint_save(self.plan, self.rank, path, self.layout, *self._ptrs(), self.t,
+                                  self.scaler.s, _stream())
+
+    def load(self, path: str) -> None:
+        """Restore what save() wrote (same plan and rank; any state layout)."""
+        meta = _abi.zero_checkpoint_load(self.plan, self.rank, path, self.layout, *self._ptrs(), _stream())
+        self.t = int(meta.step)
+        self.scaler.s = meta.scaler
+
     # -- step ----------------------------------------------------------------
-    def step(self, slices: torch.Tensor, other_ranks_sumsq: float = 0.0) -> bool:
-        """One step from an [N, ld] slice tensor; returns False if it was skipped."""
-        if slices.dim() != 2 or slices.shape[0] != self.world or slices.shape[1] < self.S:
-            raise ValueError("slices must be [N, ld >= S]")
-        if slices.dtype != self.grad_dtype or slices.stride(1) != 1:
-            raise ValueError("slices have the wrong dtype or layout")
+    def step(self, grads: torch.Tensor, other_ranks_sumsq: float = 0.0, *, full: bool = False) -> bool:
+        """One step; returns False if it was skipped.
+
+        grads: [C, ld] device tensor of C gradient buffers summed in the step and
+        divided by N -- the N ranks' slices of this shard (C = N), or one stored
+        reduce-scatter output (C = 1); with full=True, whole flat gradients in
+        the gather layout (ld >= padded numel; C = 1 is ZeRO-1's all-reduced
+        gradient).
+        """
+        need = self.plan.padded_numel if full else self.S
+        if grads.dim() != 2 or grads.shape[0] < 1 or grads.shape[1] < need:
+            raise ValueError(f"grads must be [C, ld >= {need}]")
+        if grads.dtype != self.grad_dtype or grads.stride(1) != 1:
+            raise ValueError("grads have the wrong dtype or layout")
+        if full and self.max_norm > 0:
+            raise ValueError("the clipped step reads shard buffers")
         st = _stream()
-        gcode = dtype_code(slices.dtype)
-        inv = 1.0 / self.loss_scale
+        gcode = dtype_code(grads.dtype)
+        count = int(grads.shape[0])
+        inv = self.scaler.inv_scale
         b1, b2 = self.betas
         common = dict(rank=self.rank, gather=self.gather.data_ptr(),
                       param_dtype=dtype_code(self.param_dtype), lr=self.lr, beta1=b1, beta2=b2,
                       eps=self.eps, weight_decay=self.weight_decay, step=self.t + 1)
         if self.max_norm > 0:
-            _abi.zero_reduce_shard(self.plan, slices.data_ptr(), slices.stride(0), gcode, inv,
-                                   self.g.data_ptr(), self.ws.data_ptr(), True, st)
+            _abi.zero_reduce_shard(self.plan, grads.data_ptr(), grads.stride(0), gcode, inv,
+                                   self.g.data_ptr(), self.ws.data_ptr(), True, st, grad_count=count)
             _abi.zero_shard_norm(self.plan, self.ws.data_ptr(), other_ranks_sumsq, self.max_norm,
                                  self.flag.data_ptr(), self.sumsq.data_ptr(), self.clip.data_ptr(), st)
             cur = self._state[0]
@@ -177,25 +218,19 @@ class ZeroAdam:
             ok = int(self.flag.item()) == 0
         else:
             src, dst = self._state[self._cur], self._state[1 - self._cur]
-            args = _abi.adam_args(grad=slices.data_ptr(), grad_ld=slices.stride(0), grad_dtype=gcode,
+            args = _abi.adam_args(grad=grads.data_ptr(), grad_ld=grads.stride(0), grad_dtype=gcode,
+                                  grad_count=count,
+                                  grad_layout=_abi.ZERO_GRAD_FULL if full else _abi.ZERO_GRAD_SHARD,
                                   inv_scale=inv, overflow_out=self.flag.data_ptr(),
                                   **state_arg_dict(self.layout, src, dst), **common)
             _abi.zero_adam_step(self.plan, args, st)
             ok = int(self.flag.item()) == 0
             if ok:
                 self._cur = 1 - self._cur
-        self._update_scale(ok)
-        return ok
-
-    def _update_scale(self, ok: bool) -> None:
         if ok:
             self.t += 1
-            self._clean += 1
-            if self.dynamic and self._clean >= self.growth_interval:
-                self.loss_scale *= 2.0
-                self._clean = 0
         else:
             self.skipped += 1
-            self._clean = 0
-            if self.dynamic:
-                self.loss_scale *= 0.5
+        if self.dynamic:
+            self.scaler.update(not ok)
+        return ok
