@@ -160,3 +160,90 @@ def test_full_size(name):
     if prev < pl.padded_numel:
         assert bool(torch.all(gather[prev:] == sent)), "write after the last piece"
     del A, B, gather, slices
+
+
+# The benchmark's other forms of the GPT-2 step, at full size: one stored
+# reduce-scatter output, one full all-reduced gradient (ZeRO-1), the
+# per-parameter dim-0 layout (580 pieces), and the reduction pass alone.
+VARIANTS = ["stored", "full", "dim0", "reduce_only"]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_full_size_gpt2_variants(variant):
+    import dataclasses
+    w = W.FULL["gpt2_1p5b_n8"]
+    if variant == "dim0":
+        w = dataclasses.replace(w, plan_layout="dim0")
+    pl, lay = oracle_layout(w)
+    S = lay.S
+    dev = torch.device("cuda")
+    plan = (Z.Plan.dim0([s for _n, s in w.tensors], w.world) if variant == "dim0"
+            else Z.Plan(W.numels(w.tensors), w.world, w.bucket_cap))
+    assert plan.shard_numel == S and plan.segments(w.rank) == lay.segments
+    ld = (S + 63) // 64 * 64
+    say(f"full gpt2 {variant}: S={S} pieces={len(lay.segments)}")
+    idx = _sample_idx(S, lay.segments, seed=3)
+    idx_dev = torch.from_numpy(idx).to(dev)
+    gidx = np.empty_like(idx)
+    for goff, lo, ln, _v in lay.segments:
+        sel = (idx >= lo) & (idx < lo + ln)
+        gidx[sel] = idx[sel] - lo + goff
+    gidx_dev = torch.from_numpy(gidx).to(dev)
+    st = torch.cuda.current_stream().cuda_stream
+    kw = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, t=w.t0 + 1,
+              inv_scale=1.0 / w.loss_scale)
+    if variant == "reduce_only":
+        slices = W.make_slices(w, lay, step=1, ld=ld, device=dev)
+        g = torch.empty(S, dtype=torch.float32, device=dev)
+        ws = torch.empty(plan.workspace_bytes(), dtype=torch.uint8, device=dev)
+        Z.zero_reduce_shard(plan, slices.data_ptr(), ld, CODE[w.grad_dtype], 1.0, g.data_ptr(),
+                            ws.data_ptr(), True, st)
+        torch.cuda.synchronize()
+        sl = [_take(slices[k, :S], idx_dev) for k in range(w.world)]
+        want = OS.unscale(OS.average(OS.reduce_slices(sl, w.grad_dtype), w.world), 1.0)
+        assert np.array_equal(_take(g, idx_dev).view(np.uint32), want.view(np.uint32))
+        return
+    layout, T = Z.ZERO_STATE_TILED, Z.ZERO_STATE_TILE
+    p0, m0, v0 = W.make_state(w, lay, dev)
+    A = [pack_state(p0, m0, v0, plan.state_numel(layout))]
+    del p0, m0, v0
+    B = [torch.empty_like(A[0])]
+    gather = torch.full((pl.padded_numel,), SENTINEL[w.param_dtype], dtype=W.torch_dtype(w.param_dtype),
+                        device=dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    soff = (idx // T) * 3 * T + idx % T
+    p_in, m_in, v_in = (_take(A[0], torch.from_numpy(soff + i * T).to(dev)) for i in range(3))
+    if variant == "stored":
+        grads = W.make_slices(dataclasses.replace(w, world=1), lay, step=1, ld=ld, device=dev)
+        gkw = dict(grad_ld=0, grad_count=1)
+        sl = [_take(grads[0, :S], idx_dev)]
+    elif variant == "full":
+        grads = W.make_full_grads(w, pl.padded_numel, lay.tensor_flat_off, 1, step=1, device=dev)
+        gkw = dict(grad_ld=0, grad_count=1, grad_layout=Z.ZERO_GRAD_FULL)
+        sl = [_take(grads[0], gidx_dev)]
+    else:
+        grads = W.make_slices(w, lay, step=1, ld=ld, device=dev)
+        gkw = dict(grad_ld=ld)
+        sl = [_take(grads[k, :S], idx_dev) for k in range(w.world)]
+    a = Z.adam_args(grad=grads.data_ptr(), grad_dtype=CODE[w.grad_dtype], inv_scale=1.0 / w.loss_scale,
+                    overflow_out=flag.data_ptr(), rank=w.rank, gather=gather.data_ptr(),
+                    param_dtype=CODE[w.param_dtype], lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                    weight_decay=w.weight_decay, step=w.t0 + 1, **gkw,
+                    **state_arg_dict(layout, A, B))
+    Z.zero_adam_step(plan, a, st)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    res = OS.shard_step(sl, w.grad_dtype, w.param_dtype, w.world, p_in, m_in, v_in, **kw)
+    gp, gm, gv = (_take(B[0], torch.from_numpy(soff + i * T).to(dev)) for i in range(3))
+    n, tot = compare_step(gp, gm, gv, res, p_in, m_in, v_in, res.g,
+                          OS.adam_consts(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.t0 + 1),
+                          f"gpt2 {variant}")
+    assert n == tot, f"{tot - n} sampled state elements differ in the last bit"
+    check_params(_take(gather, gidx_dev), OC.narrow(gp, w.param_dtype), w.param_dtype, f"gpt2 {variant}")
+    # nothing outside the rank's pieces was written
+    sent = torch.tensor(SENTINEL[w.param_dtype], dtype=gather.dtype, device=dev)
+    written = torch.zeros(pl.padded_numel, dtype=torch.bool, device=dev)
+    for goff, _lo, ln, _v in lay.segments:
+        written[goff:goff + ln] = True
+    assert bool(torch.all(gather[~written] == sent))
+    del A, B, gather, grads
