@@ -414,3 +414,40 @@ def test_dim0_gpt2_shapes(world, rank, n_layer, g, p, source):
 def test_dim0_clipped():
     ts = W.gpt2(n_layer=3, d=64, vocab=503, n_ctx=96)
     run_workload(_dim0(ts, 8, 5, "bf16", "bf16", max_norm=0.02), layout=TILED)
+
+
+# ---------------------------------------------------------------------------
+# seeded random configurations: layout, sizes, world, rank, dtypes, source,
+# clip and state layout drawn together
+# ---------------------------------------------------------------------------
+
+def _random_workload(seed):
+    rng = np.random.default_rng(1000 + seed)
+    world = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16, 24, 32, 64]))
+    rank = int(rng.integers(0, world))
+    g = str(rng.choice(["f32", "bf16", "f16"]))
+    p = str(rng.choice(["f32", "bf16", "f16"]))
+    dim0 = bool(rng.random() < 0.3)
+    n_t = int(rng.integers(1, 40))
+    if dim0:
+        tensors = tuple((f"t{i}", tuple(int(x) for x in rng.integers(0, 60, size=int(rng.integers(1, 3)))))
+                        for i in range(n_t))
+    else:
+        tensors = tuple((f"t{i}", (int(rng.integers(0, 3000)),)) for i in range(n_t))
+    if sum(int(np.prod(s)) for _n, s in tensors) == 0:
+        tensors = tensors + (("extra", (17,)),)
+    cap = int(rng.choice([0, 0, 500, 2000, 7000]))
+    source = str(rng.choice(["slices", "slices", "stored", "full", "full_n"]))
+    clip = source in ("slices", "stored") and rng.random() < 0.3
+    return W.Workload(name=f"random{seed}", tensors=tensors, world=world, rank=rank, bucket_cap=cap,
+                      grad_dtype=g, param_dtype=p, lr=float(rng.choice([1e-3, 3e-4, 1e-2])),
+                      weight_decay=float(rng.choice([0.0, 0.1])),
+                      loss_scale=float(rng.choice([1.0, 256.0])) if g == "f16" else 1.0,
+                      max_norm=0.01 if clip else 0.0, steps=2, seed=seed,
+                      plan_layout="dim0" if dim0 else "flat"), source, int(rng.choice([SEP, TILED]))
+
+
+@pytest.mark.parametrize("seed", range(64))
+def test_random_configurations(seed):
+    w, source, layout = _random_workload(seed)
+    run_workload(w, layout=layout, source=source)
