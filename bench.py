@@ -134,7 +134,7 @@ VARIANTS = {
 }
 
 
-def run(name, steps, warmup, with_cpu):
+def run(name, steps, warmup, with_cpu, copy_gbps=None):
     import dataclasses
 
     import torch
@@ -306,6 +306,8 @@ def run(name, steps, warmup, with_cpu):
             "step_GBps": bpe_total * S / (ms_step * 1e-3) / 1e9,
             "kernel_ms": {k: round(v[0], 5) for k, v in kernels.items()},
             "parallelism": "one rank of N (single GPU)",
+            "stream_copy_GBps": copy_gbps,
+            "dominant_kernel_of_stream_copy": (achieved / copy_gbps) if copy_gbps else None,
         },
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
@@ -317,6 +319,34 @@ def run(name, steps, warmup, with_cpu):
     del slices, A, B, gather
     torch.cuda.empty_cache()
     return out
+
+
+def device_copy_gbps(gib=2.0, launches=10) -> float:
+    """Bandwidth of the library's plain streaming copy (zero_stream_copy: the
+    step's own non-temporal 16-byte loads and stores, one read and one write
+    stream) on this GPU, bytes read + written per second: the practical ceiling
+    a streaming kernel is compared with besides the published peak."""
+    import torch
+
+    import zero_sharded_mixed_plan_amd as Z
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    st = torch.cuda.current_stream()
+    Z.zero_stream_copy(dst.data_ptr(), src.data_ptr(), 4 * n, st.cuda_stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(launches):
+        Z.zero_stream_copy(dst.data_ptr(), src.data_ptr(), 4 * n, st.cuda_stream)
+    e1.record(st)
+    torch.cuda.synchronize()
+    if not torch.equal(dst, src):
+        raise RuntimeError("zero_stream_copy produced a wrong copy")
+    ms = e0.elapsed_time(e1) / launches
+    del src, dst
+    torch.cuda.empty_cache()
+    return 8 * n / (ms * 1e-3) / 1e9
 
 
 def copy_probe(steps, warmup, gib=4.0):
@@ -375,9 +405,12 @@ def main():
     names = W.ORDER + list(VARIANTS) if args.workload == "all" else [args.workload]
     if args.workload != "all" and args.workload not in W.FULL and args.workload not in VARIANTS:
         sys.exit(f"unknown workload {args.workload}; one of {W.ORDER + list(VARIANTS)} or 'all'")
+    copy_gbps = device_copy_gbps()
+    log(f"[bench] plain streaming copy (zero_stream_copy): {copy_gbps:.0f} GB/s")
     lines = {}
     for nm in names:
-        res = run(nm, args.steps, args.warmup, with_cpu=(not args.no_cpu and nm == DEFAULT))
+        res = run(nm, args.steps, args.warmup, with_cpu=(not args.no_cpu and nm == DEFAULT),
+                  copy_gbps=copy_gbps)
         lines[nm] = res
         if len(names) > 1:
             log(json.dumps(res))

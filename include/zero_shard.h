@@ -389,6 +389,16 @@ int zero_checkpoint_save(const zero_plan_t* plan, int32_t rank, const char* path
 int zero_checkpoint_load(const zero_plan_t* plan, int32_t rank, const char* path, int32_t state_layout,
                          float* master, float* m, float* v, zero_ckpt_meta_t* meta, void* stream);
 
+/*
+ * A plain streaming copy of `bytes` bytes from src to dst (device pointers,
+ * both 16-byte aligned, bytes a multiple of 16, no overlap), with the step's
+ * own load and store forms (non-temporal 16-byte vectors, one-shot grid).  It
+ * is the practical bandwidth ceiling the step's kernels are measured against
+ * besides the published HBM peak: one read and one write stream, nothing
+ * else.  Enqueued on `stream`.  Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EHIP.
+ */
+int zero_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
 /* Message of the last error on this thread ("" if none). */
 const char* zero_last_error(void);
 

@@ -249,3 +249,13 @@ def test_args_struct_layout_matches_header(cname, pytype, tmp_path):
     assert out[0] == ctypes.sizeof(pytype)
     for f, off in zip(fields, out[1:]):
         assert getattr(pytype, f).offset == off, f
+
+
+@pytest.mark.parametrize("args,code", [((0, BASE, 64), Z.ZERO_EINVAL), ((BASE, BASE + 4096, 24), Z.ZERO_EINVAL),
+                                       ((BASE + 8, BASE + 4096, 64), Z.ZERO_EALIGN),
+                                       ((BASE, BASE + 32, 64), Z.ZERO_EINVAL),      # overlap
+                                       ((BASE, BASE + 4096, -16), Z.ZERO_EINVAL)])
+def test_stream_copy_validation(args, code):
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_stream_copy(*args)
+    assert e.value.code == code

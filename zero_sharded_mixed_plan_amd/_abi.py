@@ -29,7 +29,7 @@ EXPORTS = [
     "zero_plan_bucket", "zero_plan_tensor", "zero_plan_rank_segment", "zero_plan_bytes",
     "zero_state_numel", "zero_workspace_bytes", "zero_reduce_shard", "zero_shard_norm", "zero_adam_step",
     "zero_scaler_init", "zero_scaler_update", "zero_scaler_inv_scale", "zero_plan_hash",
-    "zero_checkpoint_save", "zero_checkpoint_load", "zero_last_error", "zero_version",
+    "zero_checkpoint_save", "zero_checkpoint_load", "zero_stream_copy", "zero_last_error", "zero_version",
 ]
 
 
@@ -136,6 +136,7 @@ def load(path: str, required: bool = True) -> ctypes.CDLL:
                                                 ctypes.POINTER(zero_ckpt_meta_t), vp]),
         "zero_checkpoint_load": (ctypes.c_int, [vp, i32, ctypes.c_char_p, i32, vp, vp, vp,
                                                 ctypes.POINTER(zero_ckpt_meta_t), vp]),
+        "zero_stream_copy": (ctypes.c_int, [vp, vp, i64, vp]),
         "zero_last_error": (ctypes.c_char_p, []),
         "zero_version": (ctypes.c_char_p, []),
     }
@@ -349,6 +350,10 @@ def zero_checkpoint_load(plan: Plan, rank: int, path: str, state_layout: int, ma
                                       master or None, m or None, v or None, ctypes.byref(meta),
                                       stream or None))
     return meta
+
+
+def zero_stream_copy(dst: int, src: int, nbytes: int, stream: int = 0) -> None:
+    _check(lib().zero_stream_copy(dst, src, int(nbytes), stream or None))
 
 
 def adam_args(**kw) -> zero_adam_args_t:

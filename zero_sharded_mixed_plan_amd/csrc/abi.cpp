@@ -354,3 +354,12 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
   }
   return ZERO_OK;
 }
+
+extern "C" int zero_stream_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+  if (!dst || !src) return fail(ZERO_EINVAL, "zero_stream_copy: NULL pointer");
+  if (bytes < 0 || bytes % 16 != 0) return fail(ZERO_EINVAL, "zero_stream_copy: bytes must be a multiple of 16");
+  if (!aligned(dst, 16) || !aligned(src, 16)) return fail(ZERO_EALIGN, "zero_stream_copy: pointers must be 16-byte aligned");
+  if (overlaps(rng(dst, bytes, "dst"), rng(src, bytes, "src")))
+    return fail(ZERO_EINVAL, "zero_stream_copy: source and destination overlap");
+  return zk::launch_stream_copy(dst, src, bytes, stream);
+}

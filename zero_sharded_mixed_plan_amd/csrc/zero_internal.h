@@ -134,6 +134,7 @@ inline size_t ws_bytes(int64_t S) {
 
 // launchers (kernels.hip); return ZERO_OK or ZERO_EHIP
 int launch_fill_u32(uint32_t* p, uint32_t value, void* stream);
+int launch_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
 int launch_step(const StepLaunch& a, zero_dtype_t gt, zero_dtype_t pt, bool stash, void* stream);
 int launch_recast(const StepLaunch& a, zero_dtype_t pt, const uint32_t* cond, void* stream);
 int launch_small_step(const StepLaunch& a, zero_dtype_t gt, zero_dtype_t pt, void* stream);
