@@ -212,10 +212,13 @@ __device__ __forceinline__ void adamw1(float& p, float& m, float& v, float g, co
   v = v2;
 }
 
-// Sum of N slices for 8 elements: acc = s_0, then acc += s_k in ascending k.
-// Software-pipelined: every load of a batch of NB slices is issued before the
-// first add, and the next batch's loads go out before this batch's adds, so a
-// wave keeps up to 2 * NB KiB in flight and never waits on one slice alone.
+// Sum of N slices for 8 elements: acc = s_0, then acc += s_k in ascending k,
+// for any N (the form used when no compile-time batch count fits, below).
+// Every load of a batch of NB slices is issued before the first add and the
+// next batch's loads go out before this batch's adds; the per-slice guards and
+// the copy of the next batch into the current one make the compiler wait for
+// all outstanding loads before each batch, so this form keeps at most two
+// batches in flight and drains between them.
 template <class T, int NB>
 __device__ __forceinline__ void reduce8(const char* base, int64_t ld_bytes, int n, float acc[8]) {
   Raw<T> cur[NB], nxt[NB];
