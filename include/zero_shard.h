@@ -371,12 +371,16 @@ typedef struct zero_ckpt_meta {
  * backoff_factor at 60; i32 growth_interval at 64; u32 0 at 68; u64 FNV-1a
  * of the master, m and v bytes at 72, 80 and 88; zeros to 128.
  *
- * save: the state (device pointers, layout as for zero_adam_step: TILED takes
+ * save: meta must be consistent (as checked on load, below).  The state
+ * (device pointers, layout as for zero_adam_step: TILED takes
  * master only, m and v NULL) is copied to host on `stream` after the work
  * already queued there, in chunks through pinned host staging, and written to
  * `path` + ".tmp", which then replaces `path`.  Returns after the file is
  * complete.
- * load: checks the header against the plan (hash, world, S) and rank, then
+ * load: checks the header against the plan (hash, world, S) and rank and its
+ * step and loss-scale fields for consistency (step >= 0, scale finite and >=
+ * 0, growth_factor > 1, backoff_factor in (0, 1), 0 <= growth_tracker <
+ * growth_interval), then
  * copies the shard into the device state on `stream` and waits for it.  A
  * checksum mismatch is found only after the data has been copied: then the
  * device state is undefined and ZERO_EIO is returned.

@@ -83,6 +83,20 @@ def test_checkpoint_save_rejects(over, code, tmp_path):
     assert not os.path.exists(tmp_path / "x") and not os.path.exists(tmp_path / "x.tmp")
 
 
+def test_checkpoint_save_rejects_inconsistent_meta(tmp_path):
+    plan = Z.Plan([100], 4)
+    bad = Z.Scaler().s
+    bad.growth_tracker = bad.growth_interval
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_checkpoint_save(plan, 1, str(tmp_path / "x"), Z.ZERO_STATE_SEPARATE, BASE, BASE + (1 << 32),
+                               BASE + (2 << 32), 3, bad)
+    assert e.value.code == Z.ZERO_EINVAL
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_checkpoint_save(plan, 1, str(tmp_path / "x"), Z.ZERO_STATE_SEPARATE, BASE, BASE + (1 << 32),
+                               BASE + (2 << 32), -1, Z.Scaler().s)
+    assert e.value.code == Z.ZERO_EINVAL
+
+
 def _load(plan, path, rank=1):
     return Z.zero_checkpoint_load(plan, rank, path, Z.ZERO_STATE_SEPARATE, BASE, BASE + (1 << 32),
                                   BASE + (2 << 32))
@@ -91,7 +105,8 @@ def _load(plan, path, rank=1):
 @pytest.mark.parametrize("case,code", [
     ("missing", Z.ZERO_EIO), ("magic", Z.ZERO_EIO), ("version", Z.ZERO_EIO), ("short", Z.ZERO_EIO),
     ("hash", Z.ZERO_EINVAL), ("world", Z.ZERO_EINVAL), ("S", Z.ZERO_EINVAL), ("rank", Z.ZERO_EINVAL),
-    ("size", Z.ZERO_EIO),
+    ("size", Z.ZERO_EIO), ("tracker", Z.ZERO_EIO), ("interval", Z.ZERO_EIO), ("backoff", Z.ZERO_EIO),
+    ("scale", Z.ZERO_EIO),
 ])
 def test_checkpoint_load_rejects_foreign_files(case, code, tmp_path):
     """Files that do not belong to this plan and rank are refused from the
@@ -114,6 +129,14 @@ def test_checkpoint_load_rejects_foreign_files(case, code, tmp_path):
         kw["rank"] = 2
     elif case == "size":
         body = body[:-4]
+    elif case == "tracker":
+        kw.update(tracker=2000, interval=2000)
+    elif case == "interval":
+        kw.update(interval=0)
+    elif case == "backoff":
+        kw.update(backoff=1.5)
+    elif case == "scale":
+        kw.update(scale=float("nan"))
     path = tmp_path / "shard"
     if case != "missing":
         data = header(**kw) + body

@@ -188,6 +188,14 @@ extern "C" int zero_checkpoint_save(const zero_plan_t* plan, int32_t rank, const
   int rc = check_state_args(fn, plan, rank, path, state_layout, master, m, v);
   if (rc) return rc;
   if (!meta) return fail(ZERO_EINVAL, std::string(fn) + ": meta is NULL");
+  {
+    const zero_scaler_t& c = meta->scaler;
+    if (meta->step < 0 || !(c.scale >= 0.0f && std::isfinite(c.scale)) ||
+        !(c.growth_factor > 1.0f && std::isfinite(c.growth_factor)) ||
+        !(c.backoff_factor > 0.0f && c.backoff_factor < 1.0f) || c.growth_interval < 1 || c.growth_tracker < 0 ||
+        c.growth_tracker >= c.growth_interval)
+      return fail(ZERO_EINVAL, std::string(fn) + ": inconsistent step or loss-scale state");
+  }
   const int64_t S = plan->shard;
   const bool tiled = state_layout == ZERO_STATE_TILED;
   hipStream_t st = (hipStream_t)stream;
@@ -277,6 +285,13 @@ extern "C" int zero_checkpoint_load(const zero_plan_t* plan, int32_t rank, const
   if (get_u64(h, 16) != zero_plan_hash(plan) || (int32_t)get_u32(h, 24) != plan->world ||
       (int64_t)get_u64(h, 32) != S)
     return fail(ZERO_EINVAL, std::string(fn) + ": the file was written for another plan");
+  {
+    const float sc = get_f32(h, 48), gf = get_f32(h, 56), bf = get_f32(h, 60);
+    const int32_t tr = (int32_t)get_u32(h, 52), gi = (int32_t)get_u32(h, 64);
+    if (!(sc >= 0.0f && std::isfinite(sc)) || !(gf > 1.0f && std::isfinite(gf)) || !(bf > 0.0f && bf < 1.0f) ||
+        gi < 1 || tr < 0 || tr >= gi || get_u32(h, 68) != 0 || (int64_t)get_u64(h, 40) < 0)
+      return fail(ZERO_EIO, std::string(fn) + ": corrupt header (step or loss-scale fields)");
+  }
   if ((int32_t)get_u32(h, 28) != rank)
     return fail(ZERO_EINVAL, std::string(fn) + ": the file holds rank " + std::to_string(get_u32(h, 28)) +
                                  "'s shard");
