@@ -198,22 +198,27 @@ typedef enum zero_grad_layout {
  * needs the norm of the whole gradient before any element is updated).
  *
  * For every local element j < S, with C = grad_count (0 means N):
- *   acc = slice_0[j] + slice_1[j] + ... + slice_{C-1}[j]   (fp32, ascending k)
+ *   acc = buf_0[j] + buf_1[j] + ... + buf_{C-1}[j]           (fp32, ascending k)
  *   g   = (acc / N) * inv_scale                              (zero_adam.py g /= world;
  *                                                             GradScaler unscale)
- * Slice k (ZERO_GRAD_SHARD layout, [S]) starts at grad + k * grad_ld elements
- * (dtype grad_dtype), 16-byte aligned start; with C > 1, ld >= S and ld a
- * 16-byte multiple (ignored when C == 1).  C == 1 reads a stored
- * reduce-scatter output (already summed over the ranks).  If g_out != NULL, g
- * is stored there (fp32, [S], 16-byte aligned).  Per workgroup, an overflow
- * word (any non-finite g) and, if want_sumsq, the float64 sum of g^2 go to
- * `ws` (zero_workspace_bytes).  The partition of elements over workgroups
- * depends only on S, so the sums are deterministic run to run.
+ * Buffer k starts at grad + k * grad_ld elements (dtype grad_dtype); the
+ * stride matters only when C > 1 and must then be a 16-byte multiple at least
+ * one buffer long.  grad_layout ZERO_GRAD_SHARD: [S] buffers, 16-byte aligned
+ * (C == 1: a stored reduce-scatter output, already summed over the ranks).
+ * ZERO_GRAD_FULL: whole flat gradients of zero_plan_padded_numel elements, read
+ * at rank `rank`'s gather offsets (ZeRO-1), element aligned; the work is then
+ * split into launches over runs of 2048-element tiles that touch at most 192
+ * pieces, and a layout with more pieces inside one tile is refused.  `rank`
+ * is used by the full layout only.  If g_out != NULL, g is stored there (fp32,
+ * [S], 16-byte aligned).  Per 2048-element tile, an overflow word (any
+ * non-finite g) and, if want_sumsq, the float64 sum of g^2 go to `ws`
+ * (zero_workspace_bytes).  The partition of elements over tiles depends only
+ * on S, so the sums are deterministic run to run.
  * Errors: ZERO_EINVAL (incl. C < 0), ZERO_EALIGN, ZERO_EHIP.
  */
-int zero_reduce_shard(const zero_plan_t* plan, const void* grad, int64_t grad_ld,
-                      int32_t grad_count, zero_dtype_t grad_dtype, float inv_scale, float* g_out,
-                      void* ws, int32_t want_sumsq, void* stream);
+int zero_reduce_shard(const zero_plan_t* plan, int32_t rank, const void* grad, int64_t grad_ld,
+                      int32_t grad_count, int32_t grad_layout, zero_dtype_t grad_dtype, float inv_scale,
+                      float* g_out, void* ws, int32_t want_sumsq, void* stream);
 
 /*
  * Second pass: finalize what zero_reduce_shard left in `ws` (two small launches:

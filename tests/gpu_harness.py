@@ -194,11 +194,12 @@ class Rig:
                         skip_in=skip, **self.state_args(src, dst), **self.common(t))
         Z.zero_adam_step(self.plan, a, torch.cuda.current_stream().cuda_stream)
 
-    def reduce_norm(self, sl_dev, other=0.0, max_norm=None, count=0):
+    def reduce_norm(self, sl_dev, other=0.0, max_norm=None, count=0, layout=Z.ZERO_GRAD_SHARD, ld=None):
         st = torch.cuda.current_stream().cuda_stream
-        Z.zero_reduce_shard(self.plan, sl_dev.data_ptr(), self.ld, CODE[self.w.grad_dtype],
-                            1.0 / self.w.loss_scale, self.g.data_ptr(), self.ws.data_ptr(), True, st,
-                            grad_count=count)
+        Z.zero_reduce_shard(self.plan, sl_dev.data_ptr(), self.ld if ld is None else ld,
+                            CODE[self.w.grad_dtype], 1.0 / self.w.loss_scale, self.g.data_ptr(),
+                            self.ws.data_ptr(), True, st, grad_count=count, grad_layout=layout,
+                            rank=self.w.rank)
         Z.zero_shard_norm(self.plan, self.ws.data_ptr(), other,
                           self.w.max_norm if max_norm is None else max_norm, self.flag.data_ptr(),
                           self.sumsq.data_ptr(), self.clip.data_ptr(), st)

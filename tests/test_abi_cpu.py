@@ -202,6 +202,20 @@ def test_reduce_and_norm_validation():
     assert e.value.code == Z.ZERO_EINVAL
 
 
+def test_reduce_refuses_a_tile_with_too_many_pieces():
+    """Full-gradient layout, 300 one-element pieces in the first 2048-element
+    tile: refused before anything is enqueued."""
+    plan = Z.Plan.dim0([(1,)] * 300 + [(5000,)], 2)
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_reduce_shard(plan, BASE, 0, Z.ZERO_BF16, 1.0, 0, BASE + (1 << 32), True, grad_count=1,
+                            grad_layout=Z.ZERO_GRAD_FULL, rank=1)
+    assert e.value.code == Z.ZERO_EINVAL and "pieces" in Z.zero_last_error()
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_reduce_shard(plan, BASE, 0, Z.ZERO_BF16, 1.0, 0, BASE + (1 << 32), True, grad_count=1,
+                            grad_layout=Z.ZERO_GRAD_FULL, rank=2)
+    assert e.value.code == Z.ZERO_EINVAL and "rank" in Z.zero_last_error()
+
+
 def test_state_numel():
     p = Z.Plan([10_000], 4)          # S = 2500 -> 2 tiles of 2048
     assert p.state_numel(Z.ZERO_STATE_SEPARATE) == 2500

@@ -70,8 +70,7 @@ def run_workload(w: W.Workload, ld_align=64, rank=None, steps=None, layout=SEP, 
         kw = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
                   t=t + 1, inv_scale=1.0 / w.loss_scale)
         if w.max_norm > 0:
-            assert source in ("slices", "stored"), "the clipped path reads shard buffers"
-            rig.reduce_norm(sl_dev, count=gkw.get("count", 0))
+            rig.reduce_norm(sl_dev, **gkw)
             torch.cuda.synchronize()
             g_ref = OS.unscale(OS.average(OS.reduce_slices(sl, w.grad_dtype), w.world),
                                1.0 / w.loss_scale)
@@ -438,7 +437,7 @@ def _random_workload(seed):
         tensors = tensors + (("extra", (17,)),)
     cap = int(rng.choice([0, 0, 500, 2000, 7000]))
     source = str(rng.choice(["slices", "slices", "stored", "full", "full_n"]))
-    clip = source in ("slices", "stored") and rng.random() < 0.3
+    clip = rng.random() < 0.3
     return W.Workload(name=f"random{seed}", tensors=tensors, world=world, rank=rank, bucket_cap=cap,
                       grad_dtype=g, param_dtype=p, lr=float(rng.choice([1e-3, 3e-4, 1e-2])),
                       weight_decay=float(rng.choice([0.0, 0.1])),
@@ -451,3 +450,19 @@ def _random_workload(seed):
 def test_random_configurations(seed):
     w, source, layout = _random_workload(seed)
     run_workload(w, layout=layout, source=source)
+
+
+@pytest.mark.parametrize("case", ["ragged", "dim0_many", "flat"])
+def test_full_gradient_clipped(case):
+    """ZeRO-1 with global-norm clipping: the reduction pass reads the rank's
+    pieces of the full gradient (several launches when the pieces exceed one
+    launch's 192)."""
+    if case == "ragged":
+        w = _ragged(4, 2, "bf16", "bf16", 70, 97, 150)
+    elif case == "dim0_many":
+        w = _dim0(W.gpt2(n_layer=20, d=64, vocab=503, n_ctx=96), 8, 5, "bf16", "bf16")
+    else:
+        w = _ragged(8, 7, "f16", "f16", 1, 100_003, 0)
+    w = dataclasses.replace(w, max_norm=0.02)
+    for layout in (SEP, TILED):
+        run_workload(w, layout=layout, source="full")

@@ -2,6 +2,7 @@
 // enqueued), fp32 step constants, and the launch sequence of each call.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <string>
@@ -84,27 +85,33 @@ void slice_consts(int32_t n, int32_t* n_pow2, float* nf, float* recip) {
 
 }  // namespace
 
-extern "C" int zero_reduce_shard(const zero_plan_t* plan, const void* grad, int64_t grad_ld,
-                                 int32_t grad_count, zero_dtype_t grad_dtype, float inv_scale, float* g_out,
-                                 void* ws, int32_t want_sumsq, void* stream) {
+extern "C" int zero_reduce_shard(const zero_plan_t* plan, int32_t rank, const void* grad, int64_t grad_ld,
+                                 int32_t grad_count, int32_t grad_layout, zero_dtype_t grad_dtype,
+                                 float inv_scale, float* g_out, void* ws, int32_t want_sumsq, void* stream) {
   if (!plan) return fail(ZERO_EINVAL, "zero_reduce_shard: plan is NULL");
   if (!ws) return fail(ZERO_EINVAL, "zero_reduce_shard: workspace is NULL");
   if (!aligned(ws, 16)) return fail(ZERO_EALIGN, "zero_reduce_shard: workspace must be 16-byte aligned");
   const int64_t S = plan->shard;
   if (grad_count < 0) return fail(ZERO_EINVAL, "zero_reduce_shard: grad_count must be >= 0 (0 = N)");
+  if (grad_layout != ZERO_GRAD_SHARD && grad_layout != ZERO_GRAD_FULL)
+    return fail(ZERO_EINVAL, "zero_reduce_shard: unknown gradient layout");
+  const bool full = grad_layout == ZERO_GRAD_FULL;
+  if (full && (rank < 0 || rank >= plan->world)) return fail(ZERO_EINVAL, "zero_reduce_shard: rank out of range");
   const int32_t count = grad_count == 0 ? plan->world : grad_count;
-  int rc = check_grad("zero_reduce_shard", grad, grad_ld, count, grad_dtype, false, S);
+  const int64_t glen = full ? plan->padded : S;
+  int rc = check_grad("zero_reduce_shard", grad, grad_ld, count, grad_dtype, full, glen);
   if (rc) return rc;
   if (g_out && !aligned(g_out, 16)) return fail(ZERO_EALIGN, "zero_reduce_shard: g_out must be 16-byte aligned");
   if (!std::isfinite(inv_scale)) return fail(ZERO_EINVAL, "zero_reduce_shard: inv_scale is not finite");
   if (g_out) {
-    const Range gr = rng(grad, grad_span(grad_ld, count, S, dtype_bytes(grad_dtype)), "grad");
+    const Range gr = rng(grad, grad_span(grad_ld, count, glen, dtype_bytes(grad_dtype)), "grad");
     if (overlaps(gr, rng(g_out, S * 4, "g_out")))
       return fail(ZERO_EINVAL, "zero_reduce_shard: g_out overlaps the slices");
   }
   zk::ReduceLaunch a{};
   a.grad = grad;
   a.ld_bytes = count > 1 ? grad_ld * dtype_bytes(grad_dtype) : 0;
+  a.grad_full = full ? 1 : 0;
   a.n = count;
   slice_consts(plan->world, &a.n_pow2, &a.nf, &a.recip_n);
   a.inv_scale = inv_scale;
@@ -114,7 +121,56 @@ extern "C" int zero_reduce_shard(const zero_plan_t* plan, const void* grad, int6
   a.want_sumsq = want_sumsq ? 1 : 0;
   a.S = S;
   a.nvec = (S + zk::kVec - 1) / zk::kVec;
-  return zk::launch_reduce(a, grad_dtype, zk::reduce_blocks(S), stream);
+  const int64_t nblocks = zk::reduce_blocks(S);
+  if (!full) {
+    a.blk0 = 0;
+    return zk::launch_reduce(a, grad_dtype, nblocks, stream);
+  }
+  // Full-gradient layout: launches over runs of whole tiles whose elements lie in
+  // at most kMaxSeg pieces (each workgroup still writes its own partial).
+  const auto& B = plan->buckets;
+  const int nb = (int)B.size();
+  auto first_piece = [&](int64_t j) {  // first piece whose local end is past element j
+    int lo = 0, hi = nb - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) / 2;
+      if (B[mid].local_off + B[mid].shard > j) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+  };
+  auto last_piece = [&](int64_t tt) {  // last piece holding an element of the tiles before tt
+    return first_piece(std::min<int64_t>(tt * zk::kTile, S) - 1);
+  };
+  // plan every launch first, so a layout that cannot be covered is refused
+  // before anything is enqueued
+  struct Run { int64_t t0, t1; int f, l; };
+  std::vector<Run> runs;
+  for (int64_t t = 0; t < nblocks;) {
+    const int f = first_piece(t * zk::kTile);
+    if (last_piece(t + 1) - f + 1 > zk::kMaxSeg)
+      return fail(ZERO_EINVAL, "zero_reduce_shard: more than " + std::to_string(zk::kMaxSeg) +
+                                   " pieces inside one 2048-element tile of the full-gradient layout");
+    // the largest t1 whose tiles [t, t1) span at most kMaxSeg pieces
+    int64_t lo = t + 1, hi = nblocks;
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo + 1) / 2;
+      if (last_piece(mid) - f + 1 <= zk::kMaxSeg) lo = mid; else hi = mid - 1;
+    }
+    runs.push_back(Run{t, lo, f, last_piece(lo)});
+    t = lo;
+  }
+  for (const Run& r : runs) {
+    a.blk0 = r.t0;
+    a.nseg = r.l - r.f + 1;
+    for (int q = 0; q < a.nseg; ++q) {
+      const auto& P = B[r.f + q];
+      a.seg[q].end = P.local_off + P.shard;
+      a.seg[q].delta = (P.base + (int64_t)rank * P.shard) - P.local_off;
+    }
+    rc = zk::launch_reduce(a, grad_dtype, r.t1 - r.t0, stream);
+    if (rc) return rc;
+  }
+  return ZERO_OK;
 }
 
 extern "C" int zero_shard_norm(const zero_plan_t* plan, void* ws, double other_ranks_sumsq,

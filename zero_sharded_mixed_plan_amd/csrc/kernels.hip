@@ -342,7 +342,8 @@ struct SegRange {
   int s0, s1;  // pieces s0 .. s1
 };
 
-__device__ __forceinline__ SegRange wave_segs(const StepLaunch& a, int64_t lo, int64_t hi) {
+template <class LA>
+__device__ __forceinline__ SegRange wave_segs(const LA& a, int64_t lo, int64_t hi) {
   // a few pieces: scan them all (no chain of dependent argument loads)
   if (a.nseg <= kScanSeg) return SegRange{0, a.nseg - 1};
   int L = 0, R = a.nseg - 1;
@@ -360,13 +361,15 @@ __device__ __forceinline__ SegRange wave_segs(const StepLaunch& a, int64_t lo, i
 }
 
 // the wave's pieces, from its first vector index (any lane's v minus its lane)
-__device__ __forceinline__ SegRange wave_segs_v(const StepLaunch& a, int64_t v) {
+template <class LA>
+__device__ __forceinline__ SegRange wave_segs_v(const LA& a, int64_t v) {
   const int64_t w0 = uniform64(v - (int64_t)(threadIdx.x & 63));
   return wave_segs(a, w0 * kVec, (w0 + 64) * kVec);
 }
 
 // gather index offset of local element j, j inside the wave's pieces
-__device__ __forceinline__ int64_t delta_of(const StepLaunch& a, const SegRange& r, int64_t j) {
+template <class LA>
+__device__ __forceinline__ int64_t delta_of(const LA& a, const SegRange& r, int64_t j) {
   int64_t d = a.seg[r.s0].delta;
   for (int s = r.s0; s < r.s1; ++s)
     if (j >= a.seg[s].end) d = a.seg[s + 1].delta;
@@ -378,8 +381,8 @@ __device__ __forceinline__ int64_t delta_of(const StepLaunch& a, const SegRange&
 // per buffer when the 8 fall in one piece on a 16-byte boundary, else element
 // by element (a piece boundary inside the 8, or a slot that is not 16-byte
 // aligned).
-template <class GT, int NB>
-__device__ __forceinline__ void reduce8_pieces(const StepLaunch& a, const SegRange& sr, int64_t j0,
+template <class GT, int NB, class LA>
+__device__ __forceinline__ void reduce8_pieces(const LA& a, const SegRange& sr, int64_t j0,
                                                float acc[8]) {
   const char* g = static_cast<const char*>(a.grad);
   const int64_t d0 = delta_of(a, sr, j0);
@@ -394,8 +397,8 @@ __device__ __forceinline__ void reduce8_pieces(const StepLaunch& a, const SegRan
 }
 
 // the gradient of local element j in slice 0
-template <class GT>
-__device__ __forceinline__ const char* grad_elem(const StepLaunch& a, const SegRange& sr, int64_t j) {
+template <class GT, class LA>
+__device__ __forceinline__ const char* grad_elem(const LA& a, const SegRange& sr, int64_t j) {
   return static_cast<const char*>(a.grad) + (j + (a.grad_full ? delta_of(a, sr, j) : 0)) * GT::bytes;
 }
 
@@ -603,16 +606,20 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) 
   // so the partition (and every partial sum) depends only on S
   double sq = 0.0;
   bool bad = false;
-  const int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t blk = a.blk0 + blockIdx.x;   // this launch's tiles start at blk0
+  const int64_t v = blk * kThreads + threadIdx.x;
   if (v < a.nvec) {
     const int64_t j0 = v * kVec;
+    const SegRange sr = wave_segs_v(a, v);
     if (j0 + kVec <= a.S) {
       float acc[8], g[8];
       constexpr int NB = Batch<GT, WIDE>::value;
       if constexpr (NBATCH > 0) {
-        const char* ubase = static_cast<const char*>(a.grad) + (int64_t)blockIdx.x * (kTile * GT::bytes);
+        const char* ubase = static_cast<const char*>(a.grad) + blk * (kTile * GT::bytes);
         reduce8_fixed<GT, NB, NBATCH>(ubase, a.ld_bytes, threadIdx.x * (uint32_t)(kVec * GT::bytes), acc,
                                       [] {});
+      } else if (a.grad_full) {
+        reduce8_pieces<GT, NB>(a, sr, j0, acc);
       } else {
         reduce8<GT, NB>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes, a.n, acc);
       }
@@ -628,7 +635,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) 
       }
     } else {
       for (int64_t j = j0; j < a.S; ++j) {
-        const float acc = reduce1<GT>(static_cast<const char*>(a.grad) + j * GT::bytes, a.ld_bytes, a.n);
+        const float acc = reduce1<GT>(grad_elem<GT>(a, sr, j), a.ld_bytes, a.n);
         const float g = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, a.inv_scale);
         bad |= !__builtin_isfinite(g);
         if (a.g_out != nullptr) a.g_out[j] = g;
@@ -655,8 +662,8 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) 
       t += s_sum[w];
       f |= s_bad[w];
     }
-    a.ws_sums[blockIdx.x] = t;
-    a.ws_flags[blockIdx.x] = f;
+    a.ws_sums[blk] = t;
+    a.ws_flags[blk] = f;
   }
 }
 
@@ -915,7 +922,7 @@ int launch_recast(const StepLaunch& a, zero_dtype_t pt, const u32* cond, void* s
 template <class GT, bool WIDE>
 static void go_reduce(const ReduceLaunch& a, dim3 grid, size_t lds, hipStream_t st) {
   constexpr int NB = Batch<GT, WIDE>::value;
-  const int nbatch = a.n % NB == 0 ? a.n / NB : 0;
+  const int nbatch = (!a.grad_full && a.n % NB == 0) ? a.n / NB : 0;
   const dim3 blk(kThreads);
   switch (nbatch) {
     case 1: hipLaunchKernelGGL((reduce_kernel<GT, WIDE, 1>), grid, blk, lds, st, a); return;

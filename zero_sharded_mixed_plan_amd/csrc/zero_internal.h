@@ -94,6 +94,7 @@ static_assert(sizeof(StepLaunch) <= 3584, "StepLaunch must fit the kernel-argume
 struct ReduceLaunch {
   const void* grad;
   int64_t ld_bytes;
+  int32_t grad_full;      // slices are full flat gradients read at the gather offsets
   int32_t n;              // slices summed (the divisor is the world size, in nf)
   int32_t n_pow2;
   float nf, recip_n, inv_scale;
@@ -103,7 +104,12 @@ struct ReduceLaunch {
   int32_t want_sumsq;
   int64_t S;
   int64_t nvec;           // ceil(S / kVec)
+  int64_t blk0;           // first tile (workgroup) of this launch
+  int32_t nseg;           // pieces of this launch's tiles (full-gradient layout)
+  Seg seg[kMaxSeg];
 };
+
+static_assert(sizeof(ReduceLaunch) <= 3584, "ReduceLaunch must fit the kernel-argument segment");
 
 struct NormLaunch {
   const uint32_t* ws_flags;

@@ -195,8 +195,6 @@ class ZeroAdam:
             raise ValueError(f"grads must be [C, ld >= {need}]")
         if grads.dtype != self.grad_dtype or grads.stride(1) != 1:
             raise ValueError("grads have the wrong dtype or layout")
-        if full and self.max_norm > 0:
-            raise ValueError("the clipped step reads shard buffers")
         st = _stream()
         gcode = dtype_code(grads.dtype)
         count = int(grads.shape[0])
@@ -207,7 +205,9 @@ class ZeroAdam:
                       eps=self.eps, weight_decay=self.weight_decay, step=self.t + 1)
         if self.max_norm > 0:
             _abi.zero_reduce_shard(self.plan, grads.data_ptr(), grads.stride(0), gcode, inv,
-                                   self.g.data_ptr(), self.ws.data_ptr(), True, st, grad_count=count)
+                                   self.g.data_ptr(), self.ws.data_ptr(), True, st, grad_count=count,
+                                   grad_layout=_abi.ZERO_GRAD_FULL if full else _abi.ZERO_GRAD_SHARD,
+                                   rank=self.rank)
             _abi.zero_shard_norm(self.plan, self.ws.data_ptr(), other_ranks_sumsq, self.max_norm,
                                  self.flag.data_ptr(), self.sumsq.data_ptr(), self.clip.data_ptr(), st)
             cur = self._state[0]
