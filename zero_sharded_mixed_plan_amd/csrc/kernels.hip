@@ -610,7 +610,8 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) 
   const int64_t v = blk * kThreads + threadIdx.x;
   if (v < a.nvec) {
     const int64_t j0 = v * kVec;
-    const SegRange sr = wave_segs_v(a, v);
+    // pieces are needed only to find the full-layout gradient
+    const SegRange sr = a.grad_full ? wave_segs_v(a, v) : SegRange{0, -1};
     if (j0 + kVec <= a.S) {
       float acc[8], g[8];
       constexpr int NB = Batch<GT, WIDE>::value;
