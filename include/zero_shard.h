@@ -193,6 +193,9 @@ typedef enum zero_grad_layout {
   ZERO_GRAD_FULL = 1
 } zero_grad_layout_t;
 
+/* Step control kept in device memory (defined with the loss-scale policy below). */
+typedef struct zero_step_ctl zero_step_ctl_t;
+
 /*
  * Gradient preparation, first pass of the clipped step (global-norm clipping
  * needs the norm of the whole gradient before any element is updated).
@@ -214,11 +217,15 @@ typedef enum zero_grad_layout {
  * non-finite g) and, if want_sumsq, the float64 sum of g^2 go to `ws`
  * (zero_workspace_bytes).  The partition of elements over tiles depends only
  * on S, so the sums are deterministic run to run.
+ * ctl (device zero_step_ctl_t, 8-byte aligned, or NULL): the loss scale is read
+ * from it on the device, inv_scale = fp32(1 / ctl->scaler.scale), and the
+ * argument inv_scale is ignored (a one-thread launch first writes ctl->k[4];
+ * *ctl is not advanced here but by the zero_adam_step that follows).
  * Errors: ZERO_EINVAL (incl. C < 0), ZERO_EALIGN, ZERO_EHIP.
  */
 int zero_reduce_shard(const zero_plan_t* plan, int32_t rank, const void* grad, int64_t grad_ld,
                       int32_t grad_count, int32_t grad_layout, zero_dtype_t grad_dtype, float inv_scale,
-                      float* g_out, void* ws, int32_t want_sumsq, void* stream);
+                      float* g_out, void* ws, int32_t want_sumsq, zero_step_ctl_t* ctl, void* stream);
 
 /*
  * Second pass: finalize what zero_reduce_shard left in `ws` (two small launches:
@@ -273,6 +280,9 @@ typedef struct zero_adam_args {
   /* optional hipEvent_t pair recorded around the main update kernel only       */
   void* ev_begin;
   void* ev_end;
+  /* optional step control in device memory: lr, step and inv_scale above are
+   * then ignored and taken from *ctl, which the call advances (see below)      */
+  zero_step_ctl_t* ctl;
 } zero_adam_args_t;
 
 /*
@@ -307,6 +317,17 @@ typedef struct zero_adam_args {
  *    touched).
  * ev_begin/ev_end (hipEvent_t or NULL) are recorded on `stream` immediately
  * before and after the main update kernel.
+ * ctl != NULL (device zero_step_ctl_t, 8-byte aligned): lr, step and
+ * inv_scale come from *ctl (t = ctl->step + 1).  The step's fp32 constants are
+ * derived from it on the device before the update and it is advanced after the
+ * update from the step's flag (overflow_out in fused mode, which is then
+ * required; skip_in in stash mode, NULL meaning applied).  This adds no launch
+ * to a fused step (the flag reset becomes the constants' launch, the restore
+ * pass advances *ctl, and the one-workgroup form for small shards does both
+ * itself) and two one-thread launches to a stash-mode step.  In fused mode a
+ * step that is not applied also copies the input state to the output arrays,
+ * so the output state is current after every call and the caller swaps the
+ * buffers unconditionally, without reading the flag.
  * Errors: ZERO_EINVAL (incl. overlapping outputs in fused mode), ZERO_EALIGN,
  * ZERO_EHIP.
  */
@@ -335,6 +356,33 @@ typedef struct zero_scaler {
   float backoff_factor;      /* in (0, 1) (0.5 by convention)                   */
   int32_t growth_interval;   /* >= 1 (2000 by convention)                       */
 } zero_scaler_t;
+
+/*
+ * Step control in device memory (zero_adam_args_t.ctl; the ctl argument of
+ * zero_reduce_shard).  It holds what changes from one step to the next -- the
+ * step count, the learning rate and the loss scale -- so that a training loop
+ * never waits for the device to learn whether a step was applied: the library
+ * computes each step's fp32 constants from it on the device, exactly as the
+ * host would (float64, rounded once; bc = 1 - beta^t with t = step + 1), and
+ * after the update a one-thread kernel reads the step's flag and advances it
+ * (step += 1 when applied, skipped += 1 otherwise, then the zero_scaler_update
+ * rule above when `dynamic` is nonzero).  A captured pair of fused steps
+ * (state A -> B, then B -> A) can then be replayed for every step of a loop.
+ * Caller-owned device memory, 8-byte aligned.  The caller writes every field
+ * but k before the first step and may rewrite any of them between steps in
+ * stream order (lr for a schedule).  The device fields are not validated:
+ * step < 0, a non-finite lr or a scale <= 0 give undefined numbers, never a
+ * fault; a scale that has underflowed to 0 makes every step overflow.
+ */
+struct zero_step_ctl {
+  int64_t step;              /* completed steps t; the next applied step uses t + 1 */
+  int64_t skipped;           /* steps not applied                                   */
+  double lr;                 /* learning rate of the next step                      */
+  zero_scaler_t scaler;      /* loss scale (inv_scale = fp32(1 / scale))            */
+  int32_t dynamic;           /* nonzero: update the scaler after every step         */
+  float k[8];                /* written by the library: bc1, bc2, lr, dec = 1-lr*wd,
+                                inv_scale of the last step begun; k[5..7] unused    */
+};
 
 /* Set *s to {init_scale, 0, growth_factor, backoff_factor, growth_interval}.
  * Errors: ZERO_EINVAL (NULL, init_scale not finite and > 0, growth_factor <= 1,

@@ -159,6 +159,10 @@ def _good(plan, **over):
     (dict(grad_layout=1, grad_ld=19_000), Z.ZERO_EINVAL),  # 4 full buffers need ld >= 19,212
     (dict(grad_layout=1, grad_count=1,                   # a full buffer reaching master_out
           grad=BASE + (4 << 32) - 64), Z.ZERO_EINVAL),
+    (dict(ctl=BASE + (9 << 32) + 4), Z.ZERO_EALIGN),      # step control must be 8-byte aligned
+    (dict(ctl=BASE + (9 << 32), overflow_out=None), Z.ZERO_EINVAL),  # fused with ctl needs the flag
+    (dict(ctl=BASE + (6 << 32) + 8), Z.ZERO_EINVAL),      # ctl inside v_out
+    (dict(ctl=BASE + (1 << 32) - 40), Z.ZERO_EINVAL),     # ctl reaching into master_in
 ])
 def test_step_validation(over, code):
     plan = Z.Plan(W.numels(W.toy_mlp()), 4)
@@ -194,6 +198,15 @@ def test_reduce_and_norm_validation():
     with pytest.raises(Z.ZeroError) as e:
         Z.zero_reduce_shard(plan, BASE, 20, Z.ZERO_BF16, 1.0, 0, BASE, True, grad_count=2)
     assert e.value.code == Z.ZERO_EINVAL          # two buffers, ld < S
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_reduce_shard(plan, BASE, 32, Z.ZERO_BF16, 1.0, 0, BASE + (1 << 32), True, ctl=BASE + (2 << 32) + 4)
+    assert e.value.code == Z.ZERO_EALIGN          # step control misaligned
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_reduce_shard(plan, BASE, 32, Z.ZERO_BF16, 1.0, 0, BASE + (1 << 32), True, ctl=BASE + (1 << 32) + 8)
+    assert e.value.code == Z.ZERO_EINVAL          # step control inside the workspace
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_reduce_shard(plan, BASE, 32, Z.ZERO_BF16, float("inf"), 0, BASE + (1 << 32), True)
+    assert e.value.code == Z.ZERO_EINVAL          # inv_scale must be finite without ctl
     with pytest.raises(Z.ZeroError) as e:
         Z.zero_shard_norm(plan, BASE, -1.0, 1.0, 0, 0, 0)
     assert e.value.code == Z.ZERO_EINVAL
@@ -239,7 +252,8 @@ def test_tiled_state_validation(over, code):
 
 @pytest.mark.parametrize("cname,pytype", [("zero_adam_args_t", Z.zero_adam_args_t),
                                            ("zero_scaler_t", Z.zero_scaler_t),
-                                           ("zero_ckpt_meta_t", Z.zero_ckpt_meta_t)])
+                                           ("zero_ckpt_meta_t", Z.zero_ckpt_meta_t),
+                                           ("zero_step_ctl_t", Z.zero_step_ctl_t)])
 def test_args_struct_layout_matches_header(cname, pytype, tmp_path):
     """The ctypes mirrors of the ABI structs have the header's field offsets
     and sizes (compiled with the host C compiler against include/zero_shard.h)."""

@@ -11,8 +11,8 @@ from ._abi import (DTYPE_BYTES, DTYPE_CODES, EXPORTS, ZERO_BF16, ZERO_EALIGN, ZE
                    ZERO_GRAD_SHARD, ZERO_OK, ZERO_STATE_SEPARATE, ZERO_STATE_TILE, ZERO_STATE_TILED,
                    Plan, Scaler, ZeroError, adam_args, lib, zero_adam_args_t, zero_adam_step,
                    zero_checkpoint_load, zero_checkpoint_save, zero_ckpt_meta_t, zero_last_error,
-                   zero_plan_hash, zero_reduce_shard, zero_scaler_t, zero_shard_norm, zero_stream_copy,
-                   zero_version)
+                   zero_plan_hash, zero_reduce_shard, zero_scaler_t, zero_shard_norm, zero_step_ctl_t,
+                   zero_stream_copy, zero_version)
 
 __all__ = [
     "DTYPE_BYTES", "DTYPE_CODES", "EXPORTS", "ZERO_BF16", "ZERO_EALIGN", "ZERO_EHIP", "ZERO_EINVAL",
@@ -20,5 +20,6 @@ __all__ = [
     "ZERO_STATE_SEPARATE", "ZERO_STATE_TILE", "ZERO_STATE_TILED", "Plan", "Scaler", "ZeroError",
     "adam_args", "lib", "zero_adam_args_t", "zero_adam_step", "zero_checkpoint_load",
     "zero_checkpoint_save", "zero_ckpt_meta_t", "zero_last_error", "zero_plan_hash",
-    "zero_reduce_shard", "zero_scaler_t", "zero_shard_norm", "zero_stream_copy", "zero_version",
+    "zero_reduce_shard", "zero_scaler_t", "zero_shard_norm", "zero_step_ctl_t", "zero_stream_copy",
+    "zero_version",
 ]

@@ -69,6 +69,7 @@ class zero_adam_args_t(ctypes.Structure):
         ("overflow_out", ctypes.c_void_p),
         ("ev_begin", ctypes.c_void_p),
         ("ev_end", ctypes.c_void_p),
+        ("ctl", ctypes.c_void_p),
     ]
 
 
@@ -79,6 +80,18 @@ class zero_scaler_t(ctypes.Structure):
         ("growth_factor", ctypes.c_float),
         ("backoff_factor", ctypes.c_float),
         ("growth_interval", ctypes.c_int32),
+    ]
+
+
+class zero_step_ctl_t(ctypes.Structure):
+    """Step control kept in device memory (this is its host image)."""
+    _fields_ = [
+        ("step", ctypes.c_int64),
+        ("skipped", ctypes.c_int64),
+        ("lr", ctypes.c_double),
+        ("scaler", zero_scaler_t),
+        ("dynamic", ctypes.c_int32),
+        ("k", ctypes.c_float * 8),
     ]
 
 
@@ -125,7 +138,7 @@ def load(path: str, required: bool = True) -> ctypes.CDLL:
         "zero_plan_bytes": (ctypes.c_int, [vp, i32, ctypes.POINTER(f64), P64]),
         "zero_state_numel": (i64, [vp, i32]),
         "zero_workspace_bytes": (ctypes.c_size_t, [vp]),
-        "zero_reduce_shard": (ctypes.c_int, [vp, i32, vp, i64, i32, i32, ctypes.c_int, f32, vp, vp, i32, vp]),
+        "zero_reduce_shard": (ctypes.c_int, [vp, i32, vp, i64, i32, i32, ctypes.c_int, f32, vp, vp, i32, vp, vp]),
         "zero_shard_norm": (ctypes.c_int, [vp, vp, f64, f64, vp, vp, vp, vp]),
         "zero_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(zero_adam_args_t), vp]),
         "zero_scaler_init": (ctypes.c_int, [ctypes.POINTER(zero_scaler_t), f32, f32, f32, i32]),
@@ -283,12 +296,15 @@ class Plan:
 
 def zero_reduce_shard(plan: Plan, grad: int, grad_ld: int, grad_dtype: int, inv_scale: float,
                       g_out: int, ws: int, want_sumsq: bool, stream: int = 0,
-                      grad_count: int = 0, grad_layout: int = ZERO_GRAD_SHARD, rank: int = 0) -> None:
+                      grad_count: int = 0, grad_layout: int = ZERO_GRAD_SHARD, rank: int = 0,
+                      ctl: int = 0) -> None:
     """grad_count: gradient buffers summed (0 = N, one per rank; 1 = a stored
     reduce-scatter output, or with grad_layout ZERO_GRAD_FULL one all-reduced
-    full gradient read at `rank`'s pieces)."""
+    full gradient read at `rank`'s pieces).  ctl: device address of a
+    zero_step_ctl_t whose loss scale replaces inv_scale (0 = none)."""
     _check(lib().zero_reduce_shard(plan.handle, int(rank), grad, grad_ld, grad_count, grad_layout, grad_dtype,
-                                   inv_scale, g_out or None, ws, 1 if want_sumsq else 0, stream or None))
+                                   inv_scale, g_out or None, ws, 1 if want_sumsq else 0, ctl or None,
+                                   stream or None))
 
 
 def zero_shard_norm(plan: Plan, ws: int, other_ranks_sumsq: float, max_norm: float,

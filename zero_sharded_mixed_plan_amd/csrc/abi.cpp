@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <cmath>
 #include <cstdio>
 #include <string>
@@ -77,6 +78,11 @@ int64_t grad_span(int64_t ld, int32_t count, int64_t len, int gb) {
   return ((int64_t)(count - 1) * ld + len) * gb;
 }
 
+// device address of ctl->k (address arithmetic only; ctl is device memory)
+const float* ctl_consts(const zero_step_ctl_t* ctl) {
+  return reinterpret_cast<const float*>(reinterpret_cast<const char*>(ctl) + offsetof(zero_step_ctl_t, k));
+}
+
 void slice_consts(int32_t n, int32_t* n_pow2, float* nf, float* recip) {
   *n_pow2 = (n & (n - 1)) == 0 ? 1 : 0;
   *nf = (float)n;
@@ -87,7 +93,8 @@ void slice_consts(int32_t n, int32_t* n_pow2, float* nf, float* recip) {
 
 extern "C" int zero_reduce_shard(const zero_plan_t* plan, int32_t rank, const void* grad, int64_t grad_ld,
                                  int32_t grad_count, int32_t grad_layout, zero_dtype_t grad_dtype,
-                                 float inv_scale, float* g_out, void* ws, int32_t want_sumsq, void* stream) {
+                                 float inv_scale, float* g_out, void* ws, int32_t want_sumsq,
+                                 zero_step_ctl_t* ctl, void* stream) {
   if (!plan) return fail(ZERO_EINVAL, "zero_reduce_shard: plan is NULL");
   if (!ws) return fail(ZERO_EINVAL, "zero_reduce_shard: workspace is NULL");
   if (!aligned(ws, 16)) return fail(ZERO_EALIGN, "zero_reduce_shard: workspace must be 16-byte aligned");
@@ -102,11 +109,16 @@ extern "C" int zero_reduce_shard(const zero_plan_t* plan, int32_t rank, const vo
   int rc = check_grad("zero_reduce_shard", grad, grad_ld, count, grad_dtype, full, glen);
   if (rc) return rc;
   if (g_out && !aligned(g_out, 16)) return fail(ZERO_EALIGN, "zero_reduce_shard: g_out must be 16-byte aligned");
-  if (!std::isfinite(inv_scale)) return fail(ZERO_EINVAL, "zero_reduce_shard: inv_scale is not finite");
-  if (g_out) {
-    const Range gr = rng(grad, grad_span(grad_ld, count, glen, dtype_bytes(grad_dtype)), "grad");
-    if (overlaps(gr, rng(g_out, S * 4, "g_out")))
-      return fail(ZERO_EINVAL, "zero_reduce_shard: g_out overlaps the slices");
+  if (!ctl && !std::isfinite(inv_scale)) return fail(ZERO_EINVAL, "zero_reduce_shard: inv_scale is not finite");
+  if (ctl && !aligned(ctl, 8)) return fail(ZERO_EALIGN, "zero_reduce_shard: ctl must be 8-byte aligned");
+  const Range gr = rng(grad, grad_span(grad_ld, count, glen, dtype_bytes(grad_dtype)), "grad");
+  if (g_out && overlaps(gr, rng(g_out, S * 4, "g_out")))
+    return fail(ZERO_EINVAL, "zero_reduce_shard: g_out overlaps the slices");
+  if (ctl) {
+    const Range cr = rng(ctl, sizeof(zero_step_ctl_t), "ctl");
+    if (overlaps(cr, gr) || (g_out && overlaps(cr, rng(g_out, S * 4, "g_out"))) ||
+        overlaps(cr, rng(ws, (int64_t)zk::ws_bytes(S), "ws")))
+      return fail(ZERO_EINVAL, "zero_reduce_shard: ctl overlaps the gradient, g_out or the workspace");
   }
   zk::ReduceLaunch a{};
   a.grad = grad;
@@ -114,7 +126,8 @@ extern "C" int zero_reduce_shard(const zero_plan_t* plan, int32_t rank, const vo
   a.grad_full = full ? 1 : 0;
   a.n = count;
   slice_consts(plan->world, &a.n_pow2, &a.nf, &a.recip_n);
-  a.inv_scale = inv_scale;
+  a.inv_scale = ctl ? 1.0f : inv_scale;
+  a.kdev = ctl ? ctl_consts(ctl) : nullptr;
   a.g_out = g_out;
   a.ws_flags = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + zk::ws_flags_offset(S));
   a.ws_sums = reinterpret_cast<double*>(static_cast<char*>(ws) + zk::ws_sums_offset());
@@ -124,6 +137,7 @@ extern "C" int zero_reduce_shard(const zero_plan_t* plan, int32_t rank, const vo
   const int64_t nblocks = zk::reduce_blocks(S);
   if (!full) {
     a.blk0 = 0;
+    if (ctl && (rc = zk::launch_ctl_begin(ctl, 0, 0.0, 0.0, 0.0, nullptr, stream))) return rc;
     return zk::launch_reduce(a, grad_dtype, nblocks, stream);
   }
   // Full-gradient layout: launches over runs of whole tiles whose elements lie in
@@ -159,6 +173,7 @@ extern "C" int zero_reduce_shard(const zero_plan_t* plan, int32_t rank, const vo
     runs.push_back(Run{t, lo, f, last_piece(lo)});
     t = lo;
   }
+  if (ctl && (rc = zk::launch_ctl_begin(ctl, 0, 0.0, 0.0, 0.0, nullptr, stream))) return rc;
   for (const Run& r : runs) {
     a.blk0 = r.t0;
     a.nseg = r.l - r.f + 1;
@@ -209,6 +224,10 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
   const int32_t N = plan->world;
   if (A.rank < 0 || A.rank >= N) return fail(ZERO_EINVAL, "zero_adam_step: rank out of range");
   const bool stash = A.g_stash != nullptr;
+  zero_step_ctl_t* const ctl = A.ctl;  // step control in device memory, or NULL
+  if (ctl && !aligned(ctl, 8)) return fail(ZERO_EALIGN, "zero_adam_step: ctl must be 8-byte aligned");
+  if (ctl && !stash && !A.overflow_out)
+    return fail(ZERO_EINVAL, "zero_adam_step: a fused step with ctl needs overflow_out");
   const int32_t count = A.grad_count == 0 ? N : A.grad_count;
   const bool full = A.grad_layout == ZERO_GRAD_FULL;
   const int64_t glen = full ? plan->padded : S;  // elements of one gradient buffer
@@ -243,17 +262,19 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
     if (A.grad_count < 0) return fail(ZERO_EINVAL, "zero_adam_step: grad_count must be >= 0 (0 = N)");
     const int rc = check_grad("zero_adam_step", A.grad, A.grad_ld, count, A.grad_dtype, full, glen);
     if (rc) return rc;
-    if (!std::isfinite(A.inv_scale)) return fail(ZERO_EINVAL, "zero_adam_step: inv_scale is not finite");
+    if (!ctl && !std::isfinite(A.inv_scale)) return fail(ZERO_EINVAL, "zero_adam_step: inv_scale is not finite");
   }
   if ((A.skip_in && !aligned(A.skip_in, 4)) || (A.overflow_out && !aligned(A.overflow_out, 4)))
     return fail(ZERO_EALIGN, "zero_adam_step: flag pointers must be 4-byte aligned");
 
-  // hyper-parameters
-  if (!(std::isfinite(A.lr) && A.lr >= 0) || !(A.beta1 >= 0 && A.beta1 < 1) ||
+  // hyper-parameters (with ctl, lr and step live in device memory)
+  const double lr = ctl ? 0.0 : A.lr;
+  const int64_t step = ctl ? 1 : A.step;
+  if (!(std::isfinite(lr) && lr >= 0) || !(A.beta1 >= 0 && A.beta1 < 1) ||
       !(A.beta2 >= 0 && A.beta2 < 1) || !(std::isfinite(A.eps) && A.eps >= 0) ||
       !std::isfinite(A.weight_decay))
     return fail(ZERO_EINVAL, "zero_adam_step: bad hyper-parameters");
-  if (A.step < 1) return fail(ZERO_EINVAL, "zero_adam_step: step counts from 1");
+  if (step < 1) return fail(ZERO_EINVAL, "zero_adam_step: step counts from 1");
 
   // aliasing: outputs never overlap each other or the gather buffer; in the
   // fused step with an overflow flag they must not overlap any input either
@@ -283,6 +304,12 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
                                      (strict ? " (a fused step with an overflow flag needs separate output state)" : ""));
     }
   }
+  if (ctl) {
+    const Range cr = rng(ctl, sizeof(zero_step_ctl_t), "ctl");
+    for (const std::vector<Range>* v : {&in_r, &out_r})
+      for (const Range& r : *v)
+        if (overlaps(cr, r)) return fail(ZERO_EINVAL, std::string("zero_adam_step: ctl overlaps ") + r.name);
+  }
 
   // fp32 constants, rounded once from float64
   zk::StepLaunch L{};
@@ -290,11 +317,11 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
   L.c.b2 = (float)A.beta2;
   L.c.omb1 = (float)(1.0 - A.beta1);
   L.c.omb2 = (float)(1.0 - A.beta2);
-  L.c.bc1 = (float)(1.0 - std::pow(A.beta1, (double)A.step));
-  L.c.bc2 = (float)(1.0 - std::pow(A.beta2, (double)A.step));
-  L.c.lr = (float)A.lr;
+  L.c.bc1 = (float)(1.0 - std::pow(A.beta1, (double)step));
+  L.c.bc2 = (float)(1.0 - std::pow(A.beta2, (double)step));
+  L.c.lr = (float)lr;
   L.c.eps = (float)A.eps;
-  L.c.dec = (float)(1.0 - A.lr * A.weight_decay);
+  L.c.dec = (float)(1.0 - lr * A.weight_decay);
   if (!(L.c.bc1 > 0.0f) || !(L.c.bc2 > 0.0f))
     return fail(ZERO_EINVAL, "zero_adam_step: bias correction rounds to 0 in fp32");
 
@@ -303,7 +330,13 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
   L.grad_full = (!stash && full) ? 1 : 0;
   L.n = stash ? N : count;
   slice_consts(N, &L.n_pow2, &L.nf, &L.recip_n);
-  L.inv_scale = A.inv_scale;
+  L.inv_scale = ctl ? 1.0f : A.inv_scale;
+  L.kdev = ctl ? ctl_consts(ctl) : nullptr;
+  L.restore = (ctl && !stash) ? 1 : 0;
+  L.ctl = nullptr;  // set on the launch that advances the step control
+  L.beta1 = A.beta1;
+  L.beta2 = A.beta2;
+  L.wd = A.weight_decay;
   L.g_stash = A.g_stash;
   L.clip = A.clip_coef;
   if (tiled) {
@@ -370,13 +403,19 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
       L.seg[s].end = B.local_off + B.shard;
       L.seg[s].delta = (B.base + (int64_t)A.rank * B.shard) - B.local_off;
     }
+    // the workgroup derives the step control's constants and advances it itself
+    L.kdev = nullptr;
+    L.ctl = ctl;
     rc = zk::record_event(A.ev_begin, stream);
     if (rc) return rc;
     rc = zk::launch_small_step(L, A.grad_dtype, A.param_dtype, stream);
     if (rc) return rc;
     return zk::record_event(A.ev_end, stream);
   }
-  if (strict) rc = zk::launch_fill_u32(A.overflow_out, 0u, stream);
+  if (ctl)  // the constants, and the flag reset of a fused step, in one launch
+    rc = zk::launch_ctl_begin(ctl, 1, A.beta1, A.beta2, A.weight_decay, strict ? A.overflow_out : nullptr, stream);
+  else if (strict)
+    rc = zk::launch_fill_u32(A.overflow_out, 0u, stream);
   if (rc) return rc;
   rc = zk::record_event(A.ev_begin, stream);
   if (rc) return rc;
@@ -396,6 +435,7 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
   if (rc) return rc;
   if (strict) {
     for (const Group& g : groups) {
+      L.ctl = (&g == &groups.back()) ? ctl : nullptr;  // the last restore pass advances the step control
       L.v_lo = g.v_lo;
       L.v_hi = g.v_hi;
       L.nseg = g.count;
@@ -408,6 +448,8 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
       if (rc) return rc;
     }
   }
+  // the fused step advanced the step control in its restore pass
+  if (ctl && stash) return zk::launch_ctl_end(ctl, A.skip_in, stream);
   return ZERO_OK;
 }
 

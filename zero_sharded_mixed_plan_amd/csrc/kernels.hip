@@ -212,6 +212,63 @@ __device__ __forceinline__ void adamw1(float& p, float& m, float& v, float g, co
   v = v2;
 }
 
+// The constants that change from step to step come from the kernel arguments,
+// or -- with the step control in device memory -- from what the begin kernel
+// wrote there for this step: bc1, bc2, lr, dec, inv_scale.  No kernel writes
+// them while a step runs, so they are read through the constant address space:
+// scalar loads, which keep them off the vector memory counters.
+typedef const __attribute__((address_space(4))) float* ConstF32;
+
+__device__ __forceinline__ void step_consts(const float* kp, AdamK& c, float& inv_scale) {
+  if (kp != nullptr) {
+    const ConstF32 k = (ConstF32)kp;
+    c.bc1 = k[0];
+    c.bc2 = k[1];
+    c.lr = k[2];
+    c.dec = k[3];
+    inv_scale = k[4];
+  }
+}
+
+// Step control in device memory: the fp32 constants of step t = ctl->step + 1
+// as the host computes them (float64, rounded once).  which = 0 or 1: the bias
+// correction 1 - beta1^t or 1 - beta2^t (two lanes of one wave evaluate the two
+// powers side by side); lr, dec = 1 - lr*wd and inv_scale = 1/scale below.
+__device__ __forceinline__ float ctl_bias_correction(const zero_step_ctl_t* ctl, int which, double beta1,
+                                                     double beta2) {
+  const double t = (double)(ctl->step + 1);
+  return (float)(1.0 - pow(which == 0 ? beta1 : beta2, t));
+}
+
+__device__ __forceinline__ float ctl_inv_scale(const zero_step_ctl_t* ctl) {
+  return (float)(1.0 / (double)ctl->scaler.scale);
+}
+
+// After a step: the step count (or the skip count), then the loss scale by the
+// host's zero_scaler_update rule.  One thread.
+__device__ __forceinline__ void ctl_advance(zero_step_ctl_t* ctl, bool skipped) {
+  if (skipped) ctl->skipped += 1;
+  else ctl->step += 1;
+  if (!ctl->dynamic) return;
+  float scale = ctl->scaler.scale;
+  int32_t tracker = ctl->scaler.growth_tracker;
+  if (skipped) {
+    scale = scale * ctl->scaler.backoff_factor;
+    tracker = 0;
+  } else {
+    const int32_t n = tracker + 1;
+    if (n >= ctl->scaler.growth_interval) {
+      const float grown = scale * ctl->scaler.growth_factor;
+      if (__builtin_isfinite(grown)) scale = grown;
+      tracker = 0;
+    } else {
+      tracker = n;
+    }
+  }
+  ctl->scaler.scale = scale;
+  ctl->scaler.growth_tracker = tracker;
+}
+
 // Sum of N slices for 8 elements: acc = s_0, then acc += s_k in ascending k,
 // for any N (the form used when no compile-time batch count fits, below).
 // Every load of a batch of NB slices is issued before the first add and the
@@ -420,6 +477,9 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
   const SegRange sr = wave_segs_v(a, v);
   float clip = 1.0f;
   if (STASH && a.clip != nullptr) clip = *a.clip;
+  AdamK c = a.c;
+  float inv_scale = a.inv_scale;
+  step_consts(a.kdev, c, inv_scale);
 
   float p[8], m[8], s[8], g[8];
   bool bad = false;
@@ -452,12 +512,12 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, a.inv_scale);
+        g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, inv_scale);
         bad |= !__builtin_isfinite(g[e]);
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) adamw1(p[e], m[e], s[e], g[e], a.c);
+    for (int e = 0; e < 8; ++e) adamw1(p[e], m[e], s[e], g[e], c);
     st8(a.p_out + o0, p);
     st8(a.m_out + o0, m);
     st8(a.v_out + o0, s);
@@ -479,10 +539,10 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
         ge = a.g_stash[j] * clip;
       } else {
         const float acc = reduce1<GT>(grad_elem<GT>(a, sr, j), a.ld_bytes, a.n);
-        ge = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, a.inv_scale);
+        ge = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, inv_scale);
         bad |= !__builtin_isfinite(ge);
       }
-      adamw1(pe, me, ve, ge, a.c);
+      adamw1(pe, me, ve, ge, c);
       a.p_out[oj] = pe;
       a.m_out[oj] = me;
       a.v_out[oj] = ve;
@@ -490,6 +550,28 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
     }
   }
   if (!STASH && a.overflow != nullptr && bad) atomicOr(a.overflow, 1u);
+}
+
+// A step that is not applied, with the step control in device memory: the
+// output state gets the input state, so the output is current either way.
+__device__ __forceinline__ void copy_state(const StepLaunch& a, int64_t j0, int cnt) {
+  if (cnt == kVec) {
+    const int64_t o0 = state_off(a, j0);
+    float x[8];
+    ld8(a.p_in + o0, x);
+    st8(a.p_out + o0, x);
+    ld8(a.m_in + o0, x);
+    st8(a.m_out + o0, x);
+    ld8(a.v_in + o0, x);
+    st8(a.v_out + o0, x);
+  } else {
+    for (int e = 0; e < cnt; ++e) {
+      const int64_t oj = state_off(a, j0 + e);
+      a.p_out[oj] = a.p_in[oj];
+      a.m_out[oj] = a.m_in[oj];
+      a.v_out[oj] = a.v_in[oj];
+    }
+  }
 }
 
 // Small shards (S <= kSmallShard) in one launch: one workgroup, one 8-element
@@ -501,9 +583,38 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
 // (batches of 8 slices whatever N: 1024 threads leave 128 registers each)
 template <class GT, class PT>
 __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLaunch a) {
+  AdamK c = a.c;
+  float inv_scale = a.inv_scale;
+  step_consts(a.kdev, c, inv_scale);
   if (a.skip_in != nullptr && *a.skip_in != 0u) {
     if (a.overflow != nullptr && threadIdx.x == 0) *a.overflow = 1u;
+    if (a.ctl != nullptr && threadIdx.x == 0) ctl_advance(a.ctl, true);
+    if (a.restore) {
+      const int64_t j = (int64_t)threadIdx.x * kVec, rest = a.S - j;
+      if (rest > 0) copy_state(a, j, rest >= kVec ? kVec : (int)rest);
+    }
     return;
+  }
+  // With the step control in device memory the workgroup derives the step's
+  // constants itself (the begin and end launches of the multi-workgroup path
+  // are folded in): every thread takes 1/scale, the last two lanes -- the
+  // least loaded, past the end of most shards -- the two powers and lr, dec,
+  // published to the others by the overflow barrier below.
+  __shared__ float s_k[4];
+  if (a.ctl != nullptr) {
+    inv_scale = ctl_inv_scale(a.ctl);
+    const int i = kSmallThreads - 1 - (int)threadIdx.x;   // 0, 1 for the last two lanes
+    if (i <= 1) {
+      const float bc = ctl_bias_correction(a.ctl, i, a.beta1, a.beta2);
+      s_k[i] = bc;
+      a.ctl->k[i] = bc;
+      if (i == 0) {
+        const double lr = a.ctl->lr;
+        s_k[2] = a.ctl->k[2] = (float)lr;
+        s_k[3] = a.ctl->k[3] = (float)(1.0 - lr * a.wd);
+        a.ctl->k[4] = inv_scale;
+      }
+    }
   }
   const int64_t j0 = (int64_t)threadIdx.x * kVec;
   const SegRange sr = wave_segs_v(a, threadIdx.x);
@@ -519,13 +630,13 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
       reduce8<GT, Batch<GT, false>::value>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes,
                                            a.n, acc);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, a.inv_scale);
+    for (int e = 0; e < 8; ++e) g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, inv_scale);
   } else {
     for (int e = 0; e < 8; ++e) {
       g[e] = 0.0f;
       if (e < cnt) {
         const float acc = reduce1<GT>(grad_elem<GT>(a, sr, j0 + e), a.ld_bytes, a.n);
-        g[e] = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, a.inv_scale);
+        g[e] = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, inv_scale);
       }
     }
   }
@@ -533,7 +644,18 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
   for (int e = 0; e < 8; ++e) bad |= !__builtin_isfinite(g[e]);
   const int any_bad = __syncthreads_or(bad ? 1 : 0);
   if (a.overflow != nullptr && threadIdx.x == 0) *a.overflow = any_bad ? 1u : 0u;
-  if (any_bad || cnt == 0) return;
+  if (a.ctl != nullptr) {
+    c.bc1 = s_k[0];
+    c.bc2 = s_k[1];
+    c.lr = s_k[2];
+    c.dec = s_k[3];
+    if (threadIdx.x == 0) ctl_advance(a.ctl, any_bad != 0);
+  }
+  if (cnt == 0) return;
+  if (any_bad) {
+    if (a.restore) copy_state(a, j0, cnt);
+    return;
+  }
   float p[8], m[8], v[8];
   if (cnt == kVec) {
     const int64_t o0 = state_off(a, j0);
@@ -541,7 +663,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
     ld8(a.m_in + o0, m);
     ld8(a.v_in + o0, v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) adamw1(p[e], m[e], v[e], g[e], a.c);
+    for (int e = 0; e < 8; ++e) adamw1(p[e], m[e], v[e], g[e], c);
     st8(a.p_out + o0, p);
     st8(a.m_out + o0, m);
     st8(a.v_out + o0, v);
@@ -556,7 +678,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
       const int64_t j = j0 + e;
       const int64_t oj = state_off(a, j);
       float pe = a.p_in[oj], me = a.m_in[oj], ve = a.v_in[oj];
-      adamw1(pe, me, ve, g[e], a.c);
+      adamw1(pe, me, ve, g[e], c);
       a.p_out[oj] = pe;
       a.m_out[oj] = me;
       a.v_out[oj] = ve;
@@ -566,14 +688,19 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
 }
 
 // On a skipped fused step: rewrite the rank's gather pieces from master_in, so
-// they keep the pre-step parameters.  A no-op unless *cond != 0.
+// they keep the pre-step parameters (and with a.restore copy the input state to
+// the output).  A no-op unless *cond != 0, apart from the step control advance
+// (a.ctl, one thread).
 template <class PT>
 __global__ __launch_bounds__(kThreads) void recast_kernel(const StepLaunch a, const u32* cond) {
-  if (*cond == 0u) return;
+  const u32 skipped = *cond;
+  if (a.ctl != nullptr && blockIdx.x == 0 && threadIdx.x == 0) ctl_advance(a.ctl, skipped != 0u);
+  if (skipped == 0u) return;
   for (int64_t v = a.v_lo + (int64_t)blockIdx.x * kThreads + threadIdx.x; v < a.v_hi;
        v += (int64_t)gridDim.x * kThreads) {
     const int64_t j0 = v * kVec;
     const SegRange sr = wave_segs_v(a, v);
+    if (a.restore) copy_state(a, j0, j0 + kVec <= a.S ? kVec : (int)(a.S - j0));
     if (j0 + kVec <= a.S) {
       float p[8];
       ld8(a.p_in + state_off(a, j0), p);
@@ -608,6 +735,9 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) 
   bool bad = false;
   const int64_t blk = a.blk0 + blockIdx.x;   // this launch's tiles start at blk0
   const int64_t v = blk * kThreads + threadIdx.x;
+  AdamK unused{};
+  float inv_scale = a.inv_scale;
+  step_consts(a.kdev, unused, inv_scale);
   if (v < a.nvec) {
     const int64_t j0 = v * kVec;
     // pieces are needed only to find the full-layout gradient
@@ -626,7 +756,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) 
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, a.inv_scale);
+        g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, inv_scale);
         bad |= !__builtin_isfinite(g[e]);
       }
       if (a.g_out != nullptr) st8_stream(a.g_out + j0, g);
@@ -637,7 +767,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) 
     } else {
       for (int64_t j = j0; j < a.S; ++j) {
         const float acc = reduce1<GT>(grad_elem<GT>(a, sr, j), a.ld_bytes, a.n);
-        const float g = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, a.inv_scale);
+        const float g = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, inv_scale);
         bad |= !__builtin_isfinite(g);
         if (a.g_out != nullptr) a.g_out[j] = g;
         if (a.want_sumsq) sq += (double)g * (double)g;
@@ -729,6 +859,29 @@ __global__ void fill_u32_kernel(u32* p, u32 value) {
   if (threadIdx.x == 0) *p = value;
 }
 
+// Step control, begin: the constants of the step about to run into ctl->k
+// (and a reset of the fused step's overflow flag, which this launch replaces).
+__global__ void ctl_begin_kernel(zero_step_ctl_t* ctl, int adam, double beta1, double beta2, double wd,
+                                 u32* reset) {
+  const int i = threadIdx.x;
+  if (i > 1) return;
+  if (adam) ctl->k[i] = ctl_bias_correction(ctl, i, beta1, beta2);
+  if (i == 0) {
+    if (adam) {
+      const double lr = ctl->lr;
+      ctl->k[2] = (float)lr;
+      ctl->k[3] = (float)(1.0 - lr * wd);
+    }
+    ctl->k[4] = ctl_inv_scale(ctl);
+    if (reset != nullptr) *reset = 0u;
+  }
+}
+
+// Step control, end: the advance after a step whose flag is *flag (NULL: applied).
+__global__ void ctl_end_kernel(zero_step_ctl_t* ctl, const u32* flag) {
+  if (threadIdx.x == 0) ctl_advance(ctl, flag != nullptr && *flag != 0u);
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -782,6 +935,18 @@ int launch_stream_copy(void* dst, const void* src, int64_t bytes, void* stream) 
 int launch_fill_u32(u32* p, u32 value, void* stream) {
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, p, value);
   return check_launch("fill");
+}
+
+int launch_ctl_begin(zero_step_ctl_t* ctl, int adam, double beta1, double beta2, double weight_decay,
+                     u32* reset_flag, void* stream) {
+  hipLaunchKernelGGL(ctl_begin_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, ctl, adam, beta1, beta2,
+                     weight_decay, reset_flag);
+  return check_launch("step control (begin)");
+}
+
+int launch_ctl_end(zero_step_ctl_t* ctl, const u32* flag, void* stream) {
+  hipLaunchKernelGGL(ctl_end_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, ctl, flag);
+  return check_launch("step control (end)");
 }
 
 // Batches of N / NB known at compile time for the world sizes that are a

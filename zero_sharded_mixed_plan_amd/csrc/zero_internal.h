@@ -79,8 +79,14 @@ struct StepLaunch {
   int64_t st_stride;
   char* gather;
   AdamK c;
+  const float* kdev;      // non-null: bc1, bc2, lr, dec, inv_scale from device memory instead
   const uint32_t* skip_in;
   uint32_t* overflow;
+  int32_t restore;        // a step that is not applied copies the input state to the output
+  // step control advanced by this launch (the one-workgroup step, which also
+  // derives its constants from it, or the last restore pass), else null
+  zero_step_ctl_t* ctl;
+  double beta1, beta2, wd;  // float64 hyper-parameters for constants derived on the device
   // local vector range of this launch and its pieces
   int64_t S;              // shard length (elements at or past S do not exist)
   int64_t v_lo, v_hi;     // vectors [v_lo, v_hi) of kVec elements
@@ -98,6 +104,7 @@ struct ReduceLaunch {
   int32_t n;              // slices summed (the divisor is the world size, in nf)
   int32_t n_pow2;
   float nf, recip_n, inv_scale;
+  const float* kdev;      // non-null: inv_scale from device memory (kdev[4]) instead
   float* g_out;
   uint32_t* ws_flags;     // [gridDim.x]
   double* ws_sums;        // [gridDim.x]
@@ -146,6 +153,12 @@ int launch_recast(const StepLaunch& a, zero_dtype_t pt, const uint32_t* cond, vo
 int launch_small_step(const StepLaunch& a, zero_dtype_t gt, zero_dtype_t pt, void* stream);
 int launch_reduce(const ReduceLaunch& a, zero_dtype_t gt, int64_t nblocks, void* stream);
 int launch_norm(const NormLaunch& a, void* stream);
+// step control in device memory: the constants of the step about to run
+// (all of them, or with adam == 0 only inv_scale; reset_flag, if given, is
+// zeroed too), and the advance after it
+int launch_ctl_begin(zero_step_ctl_t* ctl, int adam, double beta1, double beta2, double weight_decay,
+                     uint32_t* reset_flag, void* stream);
+int launch_ctl_end(zero_step_ctl_t* ctl, const uint32_t* flag, void* stream);
 int record_event(void* ev, void* stream);
 
 }  // namespace zk

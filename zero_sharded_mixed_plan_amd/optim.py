@@ -14,6 +14,7 @@ slots of `gather`, the all-gather buffer.
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional, Sequence
 
 import torch
@@ -65,6 +66,35 @@ def state_arg_dict(layout: int, src, dst) -> dict:
                 v_out=dst[2].data_ptr())
 
 
+class StepCtl:
+    """A zero_step_ctl_t in device memory: step count, skip count, learning
+    rate and loss scale that the step reads and advances on the device."""
+
+    _LR = _abi.zero_step_ctl_t.lr.offset
+
+    def __init__(self, step: int, lr: float, scaler: "_abi.zero_scaler_t", dynamic: bool, device):
+        self.buf = torch.zeros(ctypes.sizeof(_abi.zero_step_ctl_t), dtype=torch.uint8, device=device)
+        self.write(_abi.zero_step_ctl_t(step=int(step), skipped=0, lr=float(lr), scaler=scaler,
+                                        dynamic=1 if dynamic else 0))
+
+    @property
+    def ptr(self) -> int:
+        return self.buf.data_ptr()
+
+    def read(self) -> "_abi.zero_step_ctl_t":
+        """Host image, after the work queued on the current stream."""
+        return _abi.zero_step_ctl_t.from_buffer_copy(self.buf.cpu().numpy().tobytes())
+
+    def write(self, c: "_abi.zero_step_ctl_t") -> None:
+        """Replace every field, in stream order."""
+        self.buf.copy_(torch.frombuffer(bytearray(bytes(c)), dtype=torch.uint8))
+
+    def set_lr(self, lr: float) -> None:
+        """Rewrite the learning rate only, in stream order (no wait)."""
+        v = torch.tensor([float(lr)], dtype=torch.float64).view(torch.uint8)
+        self.buf[self._LR:self._LR + 8].copy_(v)
+
+
 class ZeroAdam:
     """Sharded AdamW state and step of rank `rank` out of `world`.
 
@@ -78,6 +108,12 @@ class ZeroAdam:
     layout "flat": `numels` are tensor sizes packed into flat buckets of
     `bucket_cap`; layout "dim0": `numels` are parameter shapes, each split on
     its first dimension (FSDP2 fully_shard).
+
+    device_control=True keeps the step count, the learning rate and the loss
+    scale in device memory (StepCtl): step() then never waits for the device
+    (it returns None), a skipped step leaves the output state current, and the
+    step can be captured in a HIP graph and replayed for every step.  t,
+    skipped and loss_scale read the device copy (a wait).
     """
 
     def __init__(self, numels: Sequence, world: int, rank: int, *, lr: float,
@@ -86,7 +122,8 @@ class ZeroAdam:
                  max_norm: float = 0.0, loss_scale: float = 1.0, dynamic_loss_scale: bool = False,
                  growth_interval: int = 2000, master: Optional[torch.Tensor] = None,
                  gather: Optional[torch.Tensor] = None, device="cuda",
-                 state_layout: int = _abi.ZERO_STATE_TILED, layout: str = "flat"):
+                 state_layout: int = _abi.ZERO_STATE_TILED, layout: str = "flat",
+                 device_control: bool = False):
         if layout == "dim0":
             self.plan = _abi.Plan.dim0(numels, world)
         elif layout == "flat":
@@ -94,14 +131,14 @@ class ZeroAdam:
         else:
             raise ValueError("layout must be 'flat' or 'dim0'")
         self.world, self.rank = int(world), int(rank)
-        self.lr, self.betas, self.eps, self.weight_decay = lr, tuple(betas), eps, weight_decay
+        self._lr, self.betas, self.eps, self.weight_decay = lr, tuple(betas), eps, weight_decay
         self.grad_dtype, self.param_dtype = grad_dtype, param_dtype
         self.max_norm = float(max_norm)
         self.dynamic = dynamic_loss_scale
         # a fixed scale is a scaler that is never updated
         self.scaler = _abi.Scaler(float(loss_scale), 2.0, 0.5, growth_interval)
-        self.t = 0
-        self.skipped = 0
+        self._t = 0
+        self._skipped = 0
         S = self.plan.shard_numel
         self.S = S
         dev = torch.device(device)
@@ -125,6 +162,7 @@ class ZeroAdam:
         if self.gather.numel() != self.plan.padded_numel or self.gather.dtype != param_dtype:
             raise ValueError("gather buffer has the wrong size or dtype")
         self.flag = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.ctl = StepCtl(0, lr, self.scaler.s, self.dynamic, dev) if device_control else None
         if self.max_norm > 0:
             self.g = torch.empty(S, **f32)
             self.ws = torch.empty(self.plan.workspace_bytes(), dtype=torch.uint8, device=dev)
@@ -133,7 +171,29 @@ class ZeroAdam:
 
     @property
     def loss_scale(self) -> float:
-        return self.scaler.scale
+        return self.ctl.read().scaler.scale if self.ctl else self.scaler.scale
+
+    @property
+    def t(self) -> int:
+        """Steps applied."""
+        return int(self.ctl.read().step) if self.ctl else self._t
+
+    @property
+    def skipped(self) -> int:
+        """Steps not applied (overflow)."""
+        return int(self.ctl.read().skipped) if self.ctl else self._skipped
+
+    @property
+    def lr(self) -> float:
+        return self._lr
+
+    @lr.setter
+    def lr(self, value: float) -> None:
+        """A new learning rate from the next step on (with device control, a
+        write of the device copy in stream order)."""
+        self._lr = float(value)
+        if self.ctl:
+            self.ctl.set_lr(self._lr)
 
     # -- state ---------------------------------------------------------------
     def state(self):
@@ -171,18 +231,27 @@ class ZeroAdam:
 
     def save(self, path: str) -> None:
         """Write this rank's shard (master, m, v, t, loss-scale state) to `path`."""
-        _abi.zero_checkpoint_save(self.plan, self.rank, path, self.layout, *self._ptrs(), self.t,
-                                  self.scaler.s, _stream())
+        if self.ctl:
+            c = self.ctl.read()
+            t, sc = int(c.step), c.scaler
+        else:
+            t, sc = self._t, self.scaler.s
+        _abi.zero_checkpoint_save(self.plan, self.rank, path, self.layout, *self._ptrs(), t, sc, _stream())
 
     def load(self, path: str) -> None:
         """Restore what save() wrote (same plan and rank; any state layout)."""
         meta = _abi.zero_checkpoint_load(self.plan, self.rank, path, self.layout, *self._ptrs(), _stream())
-        self.t = int(meta.step)
+        self._t = int(meta.step)
         self.scaler.s = meta.scaler
+        if self.ctl:
+            c = self.ctl.read()
+            c.step, c.scaler = meta.step, meta.scaler
+            self.ctl.write(c)
 
     # -- step ----------------------------------------------------------------
-    def step(self, grads: torch.Tensor, other_ranks_sumsq: float = 0.0, *, full: bool = False) -> bool:
-        """One step; returns False if it was skipped.
+    def step(self, grads: torch.Tensor, other_ranks_sumsq: float = 0.0, *, full: bool = False) -> Optional[bool]:
+        """One step; returns False if it was skipped (None with device control,
+        which does not wait for the device).
 
         grads: [C, ld] device tensor of C gradient buffers summed in the step and
         divided by N -- the N ranks' slices of this shard (C = N), or one stored
@@ -198,16 +267,17 @@ class ZeroAdam:
         st = _stream()
         gcode = dtype_code(grads.dtype)
         count = int(grads.shape[0])
-        inv = self.scaler.inv_scale
+        ctl = self.ctl.ptr if self.ctl else 0
+        inv = 1.0 if ctl else self.scaler.inv_scale
         b1, b2 = self.betas
         common = dict(rank=self.rank, gather=self.gather.data_ptr(),
-                      param_dtype=dtype_code(self.param_dtype), lr=self.lr, beta1=b1, beta2=b2,
-                      eps=self.eps, weight_decay=self.weight_decay, step=self.t + 1)
+                      param_dtype=dtype_code(self.param_dtype), lr=self._lr, beta1=b1, beta2=b2,
+                      eps=self.eps, weight_decay=self.weight_decay, step=self._t + 1, ctl=ctl or None)
         if self.max_norm > 0:
             _abi.zero_reduce_shard(self.plan, grads.data_ptr(), grads.stride(0), gcode, inv,
                                    self.g.data_ptr(), self.ws.data_ptr(), True, st, grad_count=count,
                                    grad_layout=_abi.ZERO_GRAD_FULL if full else _abi.ZERO_GRAD_SHARD,
-                                   rank=self.rank)
+                                   rank=self.rank, ctl=ctl)
             _abi.zero_shard_norm(self.plan, self.ws.data_ptr(), other_ranks_sumsq, self.max_norm,
                                  self.flag.data_ptr(), self.sumsq.data_ptr(), self.clip.data_ptr(), st)
             cur = self._state[0]
@@ -215,6 +285,8 @@ class ZeroAdam:
                                   skip_in=self.flag.data_ptr(),
                                   **state_arg_dict(self.layout, cur, cur), **common)
             _abi.zero_adam_step(self.plan, args, st)
+            if ctl:
+                return None
             ok = int(self.flag.item()) == 0
         else:
             src, dst = self._state[self._cur], self._state[1 - self._cur]
@@ -224,13 +296,16 @@ class ZeroAdam:
                                   inv_scale=inv, overflow_out=self.flag.data_ptr(),
                                   **state_arg_dict(self.layout, src, dst), **common)
             _abi.zero_adam_step(self.plan, args, st)
+            if ctl:                       # the output state is current either way
+                self._cur = 1 - self._cur
+                return None
             ok = int(self.flag.item()) == 0
             if ok:
                 self._cur = 1 - self._cur
         if ok:
-            self.t += 1
+            self._t += 1
         else:
-            self.skipped += 1
+            self._skipped += 1
         if self.dynamic:
             self.scaler.update(not ok)
         return ok
