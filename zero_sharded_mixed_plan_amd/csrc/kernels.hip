@@ -474,7 +474,14 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
   const int64_t v = a.v_lo + (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (v >= a.v_hi) return;
   const int64_t j0 = v * kVec;
-  const SegRange sr = wave_segs_v(a, v);
+  // The wave's pieces are needed for the parameter stores only, except where
+  // the gradient itself is read at gather offsets (the runtime-N form).  With
+  // many pieces their search is a chain of dependent argument loads, so in the
+  // compile-time batch form it runs after the vector loads have been issued,
+  // hidden behind them (the FSDP2 layout of GPT-2: -2%).
+  constexpr bool kLateSegs = !STASH && NBATCH > 0;
+  SegRange sr{0, -1};
+  if constexpr (!kLateSegs) sr = wave_segs_v(a, v);
   float clip = 1.0f;
   if (STASH && a.clip != nullptr) clip = *a.clip;
   AdamK c = a.c;
@@ -504,7 +511,10 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
         const char* ubase = static_cast<const char*>(a.grad) +
                             (a.v_lo + (int64_t)blockIdx.x * kThreads) * (kVec * GT::bytes);
         reduce8_fixed<GT, NB, NBATCH>(ubase, a.ld_bytes, threadIdx.x * (uint32_t)(kVec * GT::bytes), acc,
-                                      load_state);
+                                      [&]() {
+                                        load_state();
+                                        sr = wave_segs_v(a, v);
+                                      });
       } else {
         load_state();
         if (a.grad_full) reduce8_pieces<GT, NB>(a, sr, j0, acc);
@@ -530,6 +540,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
     }
   } else {
     // the shard's ragged end: fewer than 8 elements, element by element
+    if constexpr (kLateSegs) sr = wave_segs_v(a, v);
     for (int e = 0; e < 8; ++e) {
       const int64_t j = j0 + e;
       if (j >= a.S) break;
