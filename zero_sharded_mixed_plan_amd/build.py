@@ -39,6 +39,34 @@ def hipcc() -> str:
     return p
 
 
+# A plain C program that drives the library through include/zero_shard.h with
+# memory from the HIP runtime API alone (no Python, no torch); the GPU tests
+# run it.  Built with the host C compiler; the HIP headers need the platform
+# macro that hipcc would define.
+C_DRIVER_SRC = os.path.join(ROOT, "tests", "c", "abi_step.c")
+C_DRIVER = os.path.join(ROOT, "tests", "c", "abi_step")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_c_driver(verbose: bool = False) -> str:
+    """Compile the C driver against the built library; returns its path."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no host C compiler")
+    cmd = [cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROCM, "include"),
+           "-o", C_DRIVER + ".tmp", C_DRIVER_SRC, "-L", PKG, "-lzero_shard",
+           "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../zero_sharded_mixed_plan_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C driver build failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
+    os.replace(C_DRIVER + ".tmp", C_DRIVER)
+    return C_DRIVER
+
+
 def build(verbose: bool = False) -> str:
     """Compile the library; returns its path.  Always recompiles."""
     tmp = LIB + ".tmp"
@@ -50,6 +78,7 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_c_driver(verbose)
     return LIB
 
 
