@@ -460,15 +460,15 @@ __device__ __forceinline__ const char* grad_elem(const LA& a, const SegRange& sr
 }
 
 // ---------------------------------------------------------------------------
-// the update kernel (fused: N slices in; stash: fp32 g in)
+// the fused update kernel: N gradient buffers in
 // ---------------------------------------------------------------------------
 
-template <class GT, class PT, bool STASH, bool WIDE, int NBATCH>
+template <class GT, class PT, bool WIDE, int NBATCH>
 __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
   if (a.skip_in != nullptr && *a.skip_in != 0u) {
-    // skipped by the caller: report it like an overflow so the fused step's
-    // caller keeps its current state and the slots get their pre-step values
-    if (!STASH && a.overflow != nullptr && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.overflow, 1u);
+    // skipped by the caller: report it like an overflow so the caller keeps
+    // its current state and the slots get their pre-step values
+    if (a.overflow != nullptr && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.overflow, 1u);
     return;
   }
   const int64_t v = a.v_lo + (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -478,12 +478,12 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
   // the gradient itself is read at gather offsets (the runtime-N form).  With
   // many pieces their search is a chain of dependent argument loads, so in the
   // compile-time batch form it runs after the vector loads have been issued,
-  // hidden behind them (the FSDP2 layout of GPT-2: -2%).
-  constexpr bool kLateSegs = !STASH && NBATCH > 0;
+  // hidden behind them (the FSDP2 layout of GPT-2: -2%) -- except with four
+  // batches, where the registers are all taken by the slices in flight and the
+  // search state would spill.
+  constexpr bool kLateSegs = NBATCH == 1 || NBATCH == 2;
   SegRange sr{0, -1};
   if constexpr (!kLateSegs) sr = wave_segs_v(a, v);
-  float clip = 1.0f;
-  if (STASH && a.clip != nullptr) clip = *a.clip;
   AdamK c = a.c;
   float inv_scale = a.inv_scale;
   step_consts(a.kdev, c, inv_scale);
@@ -497,12 +497,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
       ld8(a.m_in + o0, m);
       ld8(a.v_in + o0, s);
     };
-    if (STASH) {
-      load_state();
-      ld8(a.g_stash + j0, g);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) g[e] = g[e] * clip;
-    } else {
+    {
       constexpr int NB = Batch<GT, WIDE>::value;
       float acc[8];
       if constexpr (NBATCH > 0) {
@@ -513,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
         reduce8_fixed<GT, NB, NBATCH>(ubase, a.ld_bytes, threadIdx.x * (uint32_t)(kVec * GT::bytes), acc,
                                       [&]() {
                                         load_state();
-                                        sr = wave_segs_v(a, v);
+                                        if constexpr (kLateSegs) sr = wave_segs_v(a, v);
                                       });
       } else {
         load_state();
@@ -545,14 +540,10 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
       const int64_t j = j0 + e;
       if (j >= a.S) break;
       const int64_t oj = state_off(a, j);
-      float pe = a.p_in[oj], me = a.m_in[oj], ve = a.v_in[oj], ge;
-      if (STASH) {
-        ge = a.g_stash[j] * clip;
-      } else {
-        const float acc = reduce1<GT>(grad_elem<GT>(a, sr, j), a.ld_bytes, a.n);
-        ge = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, inv_scale);
-        bad |= !__builtin_isfinite(ge);
-      }
+      float pe = a.p_in[oj], me = a.m_in[oj], ve = a.v_in[oj];
+      const float acc = reduce1<GT>(grad_elem<GT>(a, sr, j), a.ld_bytes, a.n);
+      const float ge = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, inv_scale);
+      bad |= !__builtin_isfinite(ge);
       adamw1(pe, me, ve, ge, c);
       a.p_out[oj] = pe;
       a.m_out[oj] = me;
@@ -560,7 +551,113 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
       store_param1<PT>(a.gather + (j + delta_of(a, sr, j)) * PT::bytes, pe);
     }
   }
-  if (!STASH && a.overflow != nullptr && bad) atomicOr(a.overflow, 1u);
+  if (a.overflow != nullptr && bad) atomicOr(a.overflow, 1u);
+}
+
+// ---------------------------------------------------------------------------
+// the update from the fp32 gradient stash (the clipped path's second pass)
+// ---------------------------------------------------------------------------
+
+// Four elements per lane: one 16-byte load each of g, master, m and v, so a
+// lane holds half the bytes in flight of the eight-element form (about 5%
+// faster at five resident workgroups per CU on the Llama-3 shard).  The stash
+// is read once, past the caches.
+__device__ __forceinline__ void ld4(const float* p, float o[4]) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+}
+__device__ __forceinline__ void ld4_stream(const float* p, float o[4]) {
+  const uint4 x = ld_stream16(p);
+  o[0] = __uint_as_float(x.x); o[1] = __uint_as_float(x.y); o[2] = __uint_as_float(x.z); o[3] = __uint_as_float(x.w);
+}
+__device__ __forceinline__ void st4(float* p, const float o[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+}
+
+// Store 4 parameters at dst with the widest naturally aligned stores.
+template <class PT> __device__ __forceinline__ void store_params4(char* dst, const float p[4]);
+__device__ __forceinline__ void store_words2(char* dst, u32 w0, u32 w1) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(dst);
+  if ((a & 7) == 0) {
+    st_stream8(dst, make_uint2(w0, w1));
+  } else if ((a & 3) == 0) {
+    st_stream4(dst, w0);
+    st_stream4(dst + 4, w1);
+  } else {  // 2-byte aligned 16-bit elements
+    reinterpret_cast<uint16_t*>(dst)[0] = (uint16_t)(w0 & 0xffffu);
+    reinterpret_cast<uint16_t*>(dst)[1] = (uint16_t)(w0 >> 16);
+    reinterpret_cast<uint16_t*>(dst)[2] = (uint16_t)(w1 & 0xffffu);
+    reinterpret_cast<uint16_t*>(dst)[3] = (uint16_t)(w1 >> 16);
+  }
+}
+template <> __device__ __forceinline__ void store_params4<TBF16>(char* dst, const float p[4]) {
+  store_words2(dst, pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]));
+}
+template <> __device__ __forceinline__ void store_params4<TF16>(char* dst, const float p[4]) {
+  store_words2(dst, pack_f16(p[0], p[1]), pack_f16(p[2], p[3]));
+}
+template <> __device__ __forceinline__ void store_params4<TF32>(char* dst, const float p[4]) {
+  const u32 w[4] = {__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]), __float_as_uint(p[3])};
+  const uintptr_t a = reinterpret_cast<uintptr_t>(dst);
+  if ((a & 15) == 0) {
+    st_stream16(dst, make_uint4(w[0], w[1], w[2], w[3]));
+  } else if ((a & 7) == 0) {
+    st_stream8(dst, make_uint2(w[0], w[1]));
+    st_stream8(dst + 8, make_uint2(w[2], w[3]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st_stream4(dst + 4 * i, w[i]);
+  }
+}
+
+// g = g_stash * clip_coef, then AdamW and the slot write, as in the fused form.
+// Lane t of the grid takes elements [4 q, 4 q + 4), q = 2 v_lo + t: the launch
+// covers the same 8-element vectors [v_lo, v_hi) as the fused form.  A skipped
+// step (skip_in set) writes nothing.
+template <class PT>
+__global__ __launch_bounds__(kThreads) void stash_step_kernel(const StepLaunch a) {
+  if (a.skip_in != nullptr && *a.skip_in != 0u) return;
+  const int64_t q = 2 * a.v_lo + (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t j0 = q * 4;
+  if (q >= 2 * a.v_hi || j0 >= a.S) return;
+  AdamK c = a.c;
+  float unused = 0.0f;
+  step_consts(a.kdev, c, unused);
+  const float clip = a.clip != nullptr ? *a.clip : 1.0f;
+  const int64_t w0 = uniform64(q - (int64_t)(threadIdx.x & 63));  // the wave's first group
+  if (j0 + 4 <= a.S) {
+    const int64_t o0 = state_off(a, j0);
+    float p[4], m[4], v[4], g[4];
+    ld4(a.p_in + o0, p);
+    ld4(a.m_in + o0, m);
+    ld4(a.v_in + o0, v);
+    ld4_stream(a.g_stash + j0, g);
+    const SegRange sr = wave_segs(a, w0 * 4, (w0 + 64) * 4);   // behind the loads
+#pragma unroll
+    for (int e = 0; e < 4; ++e) adamw1(p[e], m[e], v[e], g[e] * clip, c);
+    st4(a.p_out + o0, p);
+    st4(a.m_out + o0, m);
+    st4(a.v_out + o0, v);
+    const int64_t d0 = delta_of(a, sr, j0);
+    if (delta_of(a, sr, j0 + 3) == d0) {
+      store_params4<PT>(a.gather + (j0 + d0) * PT::bytes, p);
+    } else {  // the 4 elements straddle two gather pieces
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_param1<PT>(a.gather + (j0 + e + delta_of(a, sr, j0 + e)) * PT::bytes, p[e]);
+    }
+  } else {
+    // the shard's ragged end
+    const SegRange sr = wave_segs(a, w0 * 4, (w0 + 64) * 4);
+    for (int64_t j = j0; j < a.S; ++j) {
+      const int64_t oj = state_off(a, j);
+      float pe = a.p_in[oj], me = a.m_in[oj], ve = a.v_in[oj];
+      adamw1(pe, me, ve, a.g_stash[j] * clip, c);
+      a.p_out[oj] = pe;
+      a.m_out[oj] = me;
+      a.v_out[oj] = ve;
+      store_param1<PT>(a.gather + (j + delta_of(a, sr, j)) * PT::bytes, pe);
+    }
+  }
 }
 
 // A step that is not applied, with the step control in device memory: the
@@ -963,33 +1060,34 @@ int launch_ctl_end(zero_step_ctl_t* ctl, const u32* flag, void* stream) {
 // Batches of N / NB known at compile time for the world sizes that are a
 // whole number (1, 2 or 4) of batches -- 4 and 8 in narrow batches, 16, 32 and
 // 64 (fp32: 16 and 32) in wide ones; the runtime-N form for every other N.
-template <class GT, class PT, bool STASH, bool WIDE>
+template <class GT, class PT, bool WIDE>
 static void go_step_full(const StepLaunch& a, unsigned blocks, size_t lds, hipStream_t st) {
   constexpr int NB = Batch<GT, WIDE>::value;
-  const int nbatch = (!STASH && !a.grad_full && a.n % NB == 0) ? a.n / NB : 0;
+  const int nbatch = (!a.grad_full && a.n % NB == 0) ? a.n / NB : 0;
   const dim3 g(blocks), b(kThreads);
   switch (nbatch) {
-    case 1: hipLaunchKernelGGL((step_kernel<GT, PT, STASH, WIDE, 1>), g, b, lds, st, a); return;
-    case 2: hipLaunchKernelGGL((step_kernel<GT, PT, STASH, WIDE, 2>), g, b, lds, st, a); return;
-    case 4: hipLaunchKernelGGL((step_kernel<GT, PT, STASH, WIDE, 4>), g, b, lds, st, a); return;
-    default: hipLaunchKernelGGL((step_kernel<GT, PT, STASH, WIDE, 0>), g, b, lds, st, a); return;
+    case 1: hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 1>), g, b, lds, st, a); return;
+    case 2: hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 2>), g, b, lds, st, a); return;
+    case 4: hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 4>), g, b, lds, st, a); return;
+    default: hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 0>), g, b, lds, st, a); return;
   }
 }
 
 // wide batches when N > 8; the turn-taking reduction when the batch divides N
-template <class GT, class PT, bool STASH>
+template <class GT, class PT>
 static void go_step(const StepLaunch& a, unsigned blocks, size_t lds, hipStream_t st) {
-  if (!STASH && a.n > 8)
-    go_step_full<GT, PT, STASH, true>(a, blocks, lds, st);
+  if (a.n > 8)
+    go_step_full<GT, PT, true>(a, blocks, lds, st);
   else
-    go_step_full<GT, PT, STASH, false>(a, blocks, lds, st);
+    go_step_full<GT, PT, false>(a, blocks, lds, st);
 }
 
 // Resident workgroups per CU of the streaming kernels.  Fewer concurrent waves
 // keep fewer DRAM pages open per stream.  Measured on the GPT-2 1.5B and
 // Llama-7B shards, 2 workgroups (8 wave64s) per CU stream the fused update and
 // the reduction 7-8% faster than 3 or 4, while 1 per CU is too few to cover
-// the latency; the stash-mode update, with four streams, is best at 3-4.
+// the latency; the stash-mode update (four elements per lane) is best at 5
+// (2: -20%, 3: -5%, 4: -1%, 6: -1% on the Llama-3 clipped step).
 // The cap is imposed by reserving dynamic LDS the kernels do not otherwise use.
 // The reservation sits halfway between the sizes at which per_cu + 1 and
 // per_cu workgroups just fit, in 2 KiB steps, so that neither the allocation
@@ -1025,14 +1123,25 @@ static size_t occupancy_lds(int per_cu) {
 // +7% from one full all-reduced gradient).
 static int stream_blocks_per_cu(int n) { return n <= 2 ? kFewStreamBlocksPerCU : kStreamBlocksPerCU; }
 
-template <class GT, bool STASH>
+template <class GT>
 static int dispatch_pt(const StepLaunch& a, zero_dtype_t pt, unsigned blocks, hipStream_t st) {
-  // the stash-mode update moves four streams and wants one workgroup more per CU
-  const size_t lds = occupancy_lds(STASH ? kStashBlocksPerCU : stream_blocks_per_cu(a.n));
+  const size_t lds = occupancy_lds(stream_blocks_per_cu(a.n));
   switch (pt) {
-    case ZERO_F32: go_step<GT, TF32, STASH>(a, blocks, lds, st); return ZERO_OK;
-    case ZERO_BF16: go_step<GT, TBF16, STASH>(a, blocks, lds, st); return ZERO_OK;
-    case ZERO_F16: go_step<GT, TF16, STASH>(a, blocks, lds, st); return ZERO_OK;
+    case ZERO_F32: go_step<GT, TF32>(a, blocks, lds, st); return ZERO_OK;
+    case ZERO_BF16: go_step<GT, TBF16>(a, blocks, lds, st); return ZERO_OK;
+    case ZERO_F16: go_step<GT, TF16>(a, blocks, lds, st); return ZERO_OK;
+  }
+  return fail(ZERO_EINVAL, "unsupported parameter dtype");
+}
+
+// the stash-mode update: two 4-element groups per 8-element vector
+static int dispatch_stash(const StepLaunch& a, zero_dtype_t pt, int64_t nv, hipStream_t st) {
+  const dim3 g((unsigned)((2 * nv + kThreads - 1) / kThreads)), b(kThreads);
+  const size_t lds = occupancy_lds(kStashBlocksPerCU);
+  switch (pt) {
+    case ZERO_F32: hipLaunchKernelGGL(stash_step_kernel<TF32>, g, b, lds, st, a); return ZERO_OK;
+    case ZERO_BF16: hipLaunchKernelGGL(stash_step_kernel<TBF16>, g, b, lds, st, a); return ZERO_OK;
+    case ZERO_F16: hipLaunchKernelGGL(stash_step_kernel<TF16>, g, b, lds, st, a); return ZERO_OK;
   }
   return fail(ZERO_EINVAL, "unsupported parameter dtype");
 }
@@ -1044,12 +1153,12 @@ int launch_step(const StepLaunch& a, zero_dtype_t gt, zero_dtype_t pt, bool stas
   hipStream_t st = (hipStream_t)stream;
   int rc;
   if (stash) {
-    rc = dispatch_pt<TF32, true>(a, pt, blocks, st);
+    rc = dispatch_stash(a, pt, nv, st);
   } else {
     switch (gt) {
-      case ZERO_F32: rc = dispatch_pt<TF32, false>(a, pt, blocks, st); break;
-      case ZERO_BF16: rc = dispatch_pt<TBF16, false>(a, pt, blocks, st); break;
-      case ZERO_F16: rc = dispatch_pt<TF16, false>(a, pt, blocks, st); break;
+      case ZERO_F32: rc = dispatch_pt<TF32>(a, pt, blocks, st); break;
+      case ZERO_BF16: rc = dispatch_pt<TBF16>(a, pt, blocks, st); break;
+      case ZERO_F16: rc = dispatch_pt<TF16>(a, pt, blocks, st); break;
       default: return fail(ZERO_EINVAL, "unsupported gradient dtype");
     }
   }

@@ -38,7 +38,7 @@ constexpr int kNormGroups = 256;      // first-level workgroups of the norm fina
 constexpr int kStateTileShift = 11;   // tiled state: 2048 elements of master, m, v per tile
 constexpr int64_t kStateTile = int64_t(1) << kStateTileShift;
 constexpr int kStreamBlocksPerCU = 2; // resident workgroups per CU of the streaming kernels
-constexpr int kStashBlocksPerCU = 4;  // ... of the update kernel that reads the fp32 stash
+constexpr int kStashBlocksPerCU = 5;  // ... of the update kernel that reads the fp32 stash
 constexpr int kFewStreamBlocksPerCU = 3;  // ... of kernels that sum one or two gradient buffers
 constexpr size_t kStaticLdsRoom = 1024;  // LDS left for a streaming kernel's own __shared__ arrays
 constexpr int kSmallThreads = 1024;   // one-workgroup path for small shards ...
