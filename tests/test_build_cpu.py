@@ -1,0 +1,27 @@
+"""The build's kernel-resource check: the compiler's resource-usage remarks are
+parsed per kernel, and a kernel that spills to scratch fails the build."""
+from zero_sharded_mixed_plan_amd import build as B
+
+REMARKS = """\
+k.hip:10:1: remark: Function Name: _Z1av [-Rpass-analysis=kernel-resource-usage]
+k.hip:10:1: remark:     VGPRs: 30 [-Rpass-analysis=kernel-resource-usage]
+k.hip:10:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]
+k.hip:10:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]
+   10 | __global__ void a() {}
+k.hip:20:1: remark: Function Name: _Z1bv [-Rpass-analysis=kernel-resource-usage]
+k.hip:20:1: remark:     VGPRs: 256 [-Rpass-analysis=kernel-resource-usage]
+k.hip:20:1: remark:     ScratchSize [bytes/lane]: 20 [-Rpass-analysis=kernel-resource-usage]
+k.hip:20:1: remark:     VGPRs Spill: 5 [-Rpass-analysis=kernel-resource-usage]
+k.hip:30:1: warning: something else
+"""
+
+
+def test_resource_remarks_parsed_per_kernel():
+    r = B.kernel_resources(REMARKS)
+    assert set(r) == {"_Z1av", "_Z1bv"}
+    assert r["_Z1av"] == {"VGPRs": "30", "ScratchSize [bytes/lane]": "0", "VGPRs Spill": "0"}
+    assert r["_Z1bv"]["ScratchSize [bytes/lane]"] == "20" and r["_Z1bv"]["VGPRs Spill"] == "5"
+
+
+def test_the_resource_flag_is_part_of_the_build():
+    assert "-Rpass-analysis=kernel-resource-usage" in B.FLAGS

@@ -29,7 +29,10 @@ FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
+    # per-kernel registers, scratch and occupancy as compiler remarks (parsed below)
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+RESOURCES = os.path.join(PKG, "kernel_resources.txt")
 
 
 def hipcc() -> str:
@@ -67,8 +70,25 @@ def build_c_driver(verbose: bool = False) -> str:
     return C_DRIVER
 
 
+def kernel_resources(remarks: str) -> dict:
+    """{kernel: {field: value}} from the compiler's kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for line in remarks.splitlines():
+        if "remark:" not in line or "kernel-resource-usage" not in line:
+            continue
+        body = line.split("remark:", 1)[1].rsplit("[-Rpass-analysis", 1)[0].strip()
+        key, _, val = body.partition(":")
+        if key == "Function Name":
+            cur = out.setdefault(val.strip(), {})
+        elif cur is not None:
+            cur[key.strip()] = val.strip()
+    return out
+
+
 def build(verbose: bool = False) -> str:
-    """Compile the library; returns its path.  Always recompiles."""
+    """Compile the library; returns its path.  Always recompiles.  A kernel
+    that spills to scratch memory fails the build: every kernel here streams
+    from registers, and a spill has cost the step several percent."""
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
            "-o", tmp, *SOURCES]
@@ -77,6 +97,18 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
+    res = kernel_resources(r.stderr)
+    with open(RESOURCES, "w") as f:
+        for name in sorted(res):
+            f.write(name + " " + " ".join(f"{k.replace(' ', '_')}={v}" for k, v in res[name].items()) + "\n")
+    spills = [n for n, d in res.items()
+              if d.get("ScratchSize [bytes/lane]", "0") != "0" or d.get("VGPRs Spill", "0") != "0"
+              or d.get("SGPRs Spill", "0") != "0"]
+    if not res:
+        raise RuntimeError("hipcc printed no kernel resource usage")
+    if spills:
+        os.remove(tmp)
+        raise RuntimeError("kernels spill to scratch memory: " + ", ".join(sorted(spills)))
     os.replace(tmp, LIB)
     build_c_driver(verbose)
     return LIB
