@@ -687,14 +687,14 @@ template <> __device__ __forceinline__ void widen4<TF32>(const Raw4<TF32>& r, fl
   o[2] = __uint_as_float(r.q.z); o[3] = __uint_as_float(r.q.w);
 }
 
-// The fused update over C [S] gradient buffers (C = 1, 2, 4; fp32 also 8),
-// four elements per lane as in the stash-mode update: one load per buffer and
-// one each of master, m and v, all issued before the first add, then the same
-// sum, arithmetic and stores as the eight-element form.  With few buffers the
-// state dominates the traffic, and half the bytes in flight per lane streams
-// faster (GPT-2 1.5B shard: one stored output -4%, N = 2 -3%, N = 4 -12%
-// against the runtime-N loop the eight-element form uses there; fp32 gradients
-// -9%, and -8% at N = 8).  Lane t takes elements [4 q, 4 q + 4), q = 2 v_lo + t.
+// The fused update over C [S] gradient buffers, four elements per lane as in
+// the stash-mode update: one load per buffer and one each of master, m and v,
+// all issued before the first add, then the same sum (ascending k), arithmetic
+// and stores as the eight-element form.  A lane holds half the bytes in flight
+// of that form, which streams faster for most counts (GPT-2 1.5B shard: one
+// stored output -4%, N = 2 -3%, N = 4 -12%, N = 32 -8%; 7.5B N = 64 -2%;
+// Llama-7B N = 16 -6%; fp32 gradients -8 to -11%).  Lane t takes elements
+// [4 q, 4 q + 4), q = 2 v_lo + t.
 template <class GT, class PT, int C>
 __global__ __launch_bounds__(kThreads) void narrow_step_kernel(const StepLaunch a) {
   if (a.skip_in != nullptr && *a.skip_in != 0u) {
@@ -1160,19 +1160,31 @@ int launch_ctl_end(zero_step_ctl_t* ctl, const u32* flag, void* stream) {
 }
 
 // Batches of N / NB known at compile time for the world sizes that are a
-// whole number (1, 2 or 4) of batches -- 4 and 8 in narrow batches, 16, 32 and
-// 64 (fp32: 16 and 32) in wide ones; the runtime-N form for every other N.
+// whole number (1, 2 or 4) of batches and that the narrow form does not take:
+// 16-bit N = 8 in one narrow batch, fp32 N = 16 and 32 in two and four wide
+// ones; the runtime-N form for every other N and for the full-gradient source.
 template <class GT, class PT, bool WIDE>
 static void go_step_full(const StepLaunch& a, unsigned blocks, size_t lds, hipStream_t st) {
   constexpr int NB = Batch<GT, WIDE>::value;
   const int nbatch = (!a.grad_full && a.n % NB == 0) ? a.n / NB : 0;
   const dim3 g(blocks), b(kThreads);
-  switch (nbatch) {
-    case 1: hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 1>), g, b, lds, st, a); return;
-    case 2: hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 2>), g, b, lds, st, a); return;
-    case 4: hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 4>), g, b, lds, st, a); return;
-    default: hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 0>), g, b, lds, st, a); return;
+  if constexpr (GT::bytes == 2 && !WIDE) {
+    if (nbatch == 1) {
+      hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 1>), g, b, lds, st, a);
+      return;
+    }
   }
+  if constexpr (GT::bytes == 4 && WIDE) {
+    if (nbatch == 2) {
+      hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 2>), g, b, lds, st, a);
+      return;
+    }
+    if (nbatch == 4) {
+      hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 4>), g, b, lds, st, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 0>), g, b, lds, st, a);
 }
 
 // wide batches when N > 8; the turn-taking reduction when the batch divides N
@@ -1237,11 +1249,14 @@ static int dispatch_pt(const StepLaunch& a, zero_dtype_t pt, unsigned blocks, hi
 }
 
 // The narrow fused form serves the shard layout when its buffer count is
-// compiled (1, 2, 4; fp32 also 8); resident workgroups per CU: 3, or 2 when
-// a lane's raw gradient bytes exceed 64 (fp32, C = 8), as measured.
+// compiled: 1, 2, 4, and 16, 32, 64 for 16-bit gradients or 8 for fp32 (the
+// eight-element form keeps 16-bit N = 8, where the two measure the same, and
+// fp32 N >= 16).  Resident workgroups per CU: 3, or 2 when a lane's raw
+// gradient bytes exceed 64, as measured.
 static bool narrow_form(zero_dtype_t gt, int n, int grad_full) {
   if (grad_full) return false;
-  return n == 1 || n == 2 || n == 4 || (gt == ZERO_F32 && n == 8);
+  if (n == 1 || n == 2 || n == 4) return true;
+  return gt == ZERO_F32 ? n == 8 : (n == 16 || n == 32 || n == 64);
 }
 
 template <class GT, class PT>
@@ -1255,6 +1270,16 @@ static int go_narrow(const StepLaunch& a, int64_t nv, hipStream_t st) {
     case 8:
       if constexpr (GT::bytes == 4) {
         hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 8>), g, b, lds, st, a);
+        return ZERO_OK;
+      }
+      break;
+    case 16:
+    case 32:
+    case 64:
+      if constexpr (GT::bytes == 2) {
+        if (a.n == 16) hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 16>), g, b, lds, st, a);
+        else if (a.n == 32) hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 32>), g, b, lds, st, a);
+        else hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 64>), g, b, lds, st, a);
         return ZERO_OK;
       }
       break;
