@@ -166,3 +166,44 @@ def test_device_constants_match_host():
         if [F32(x) for x in k] != want:
             bad.append((t, k, want))
     assert not bad, bad[:5]
+
+
+@pytest.mark.parametrize("clip", [False, True])
+def test_sequence_many_pieces_dim0(clip):
+    """The FSDP2 dim-0 layout of a 20-layer model (more than 192 pieces per rank,
+    so the update runs in several launches and the last restore pass advances
+    the step control): five steps with an overflow, against the oracle."""
+    w = W.Workload(name="dim0_many", tensors=tuple(W.gpt2(n_layer=20, d=64, vocab=503, n_ctx=96)), world=8,
+                   rank=5, bucket_cap=0, grad_dtype="f16", param_dtype="f16", lr=1e-3, weight_decay=0.05,
+                   loss_scale=512.0, steps=5, seed=17, plan_layout="dim0", inject_inf_step=2,
+                   max_norm=(0.02 if clip else 0.0))
+    pl, lay = oracle_layout(w)
+    S = lay.S
+    assert len(lay.segments) > 192
+    master, m0, v0 = W.make_state(w, lay, "cpu")
+    opt = ZeroAdam([s for _n, s in w.tensors], w.world, w.rank, lr=w.lr, weight_decay=w.weight_decay,
+                   grad_dtype=torch.float16, param_dtype=torch.float16, max_norm=w.max_norm,
+                   loss_scale=w.loss_scale, dynamic_loss_scale=True, growth_interval=2, master=master.cuda(),
+                   layout="dim0", device_control=True)
+    say(f"device control dim0 S={S} pieces={len(lay.segments)} clip={clip}")
+    p, m, v = master.numpy(), m0.numpy(), v0.numpy()
+    t = 0
+    sc = ORS.ScalerState(scale=F32(w.loss_scale), growth_tracker=0, growth_interval=2)
+    for step in range(1, 6):
+        sl = W.make_slices(dataclasses.replace(w, loss_scale=float(sc.scale)), lay, step=step,
+                           ld=(S + 63) // 64 * 64)
+        opt.step(sl.cuda())
+        res = OS.shard_step([storage(sl[k, :S]) for k in range(w.world)], "f16", "f16", w.world, p, m, v,
+                            lr=w.lr, weight_decay=w.weight_decay, t=t + 1, inv_scale=float(ORS.inv_scale(sc)),
+                            max_norm=w.max_norm, clip_override=(F32(opt.clip.item()) if clip else None))
+        gp, gm, gv = (x.cpu().numpy() for x in opt.state())
+        for a, b, what in ((gp, res.master, "master"), (gm, res.m, "m"), (gv, res.v, "v")):
+            assert np.array_equal(_bits(a), _bits(b)), f"step {step}: {what}"
+        for goff, loff, ln, _v in lay.segments:
+            assert np.array_equal(storage(opt.gather[goff:goff + ln]), OC.narrow(gp[loff:loff + ln], "f16"))
+        if not res.flag:
+            p, m, v, t = res.master, res.m, res.v, t + 1
+        sc = ORS.update(sc, res.flag)
+        c = opt.ctl.read()
+        assert (c.step, F32(c.scaler.scale), c.scaler.growth_tracker) == (t, sc.scale, sc.growth_tracker)
+    assert opt.skipped == 1
