@@ -247,3 +247,87 @@ def test_full_size_gpt2_variants(variant):
         written[goff:goff + ln] = True
     assert bool(torch.all(gather[~written] == sent))
     del A, B, gather, grads
+
+
+@pytest.mark.parametrize("clip", [False, True])
+def test_shard_beyond_int32(clip):
+    """A shard longer than 2^31 elements (one flat tensor, N = 2, rank 1, a
+    ragged end): every index in the kernels and the host is 64-bit.  Sampled
+    elements, including a window around 2^31 and the shard's end, against the
+    oracle; the gather buffer outside the rank's piece is untouched.  About 100
+    GB of device memory at the peak."""
+    S_want = (1 << 31) + 4099
+    w = W.Workload(name="beyond_int32", tensors=(("flat", (2 * S_want - 3,)),), world=2, rank=1, bucket_cap=0,
+                   grad_dtype="bf16", param_dtype="bf16", lr=1e-3, weight_decay=0.1, steps=1, seed=29,
+                   max_norm=(0.05 if clip else 0.0))
+    pl, lay = oracle_layout(w)
+    S = lay.S
+    assert S > (1 << 31)
+    dev = torch.device("cuda")
+    plan = Z.Plan(W.numels(w.tensors), w.world, w.bucket_cap)
+    assert plan.shard_numel == S
+    ld = (S + 63) // 64 * 64
+    say(f"beyond int32: S={S} clip={clip}")
+    idx = np.unique(np.concatenate([_sample_idx(S, lay.segments, n=1 << 16, seed=5),
+                                    np.arange((1 << 31) - 64, (1 << 31) + 64)])).astype(np.int64)
+    idx_dev = torch.from_numpy(idx).to(dev)
+    gidx_dev = torch.from_numpy(idx + lay.segments[0][0]).to(dev)
+    layout, T = Z.ZERO_STATE_TILED, Z.ZERO_STATE_TILE
+    p0, m0, v0 = W.make_state(w, lay, dev)
+    A = [pack_state(p0, m0, v0, plan.state_numel(layout))]
+    del p0, m0, v0
+    torch.cuda.empty_cache()
+    soff = (idx // T) * 3 * T + idx % T
+    soff_dev = [torch.from_numpy(soff + i * T).to(dev) for i in range(3)]
+    p_in, m_in, v_in = (_take(A[0], soff_dev[i]) for i in range(3))
+    gather = torch.full((pl.padded_numel,), SENTINEL["bf16"], dtype=torch.bfloat16, device=dev)
+    slices = W.make_slices(w, lay, step=1, ld=ld, device=dev)
+    sl = [_take(slices[k, :S], idx_dev) for k in range(w.world)]
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+    common = dict(rank=w.rank, gather=gather.data_ptr(), param_dtype=CODE["bf16"], lr=w.lr, beta1=w.beta1,
+                  beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=w.t0 + 1)
+    kw = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, t=w.t0 + 1,
+              inv_scale=1.0)
+    say("  inputs ready")
+    if clip:
+        g = torch.empty(S, dtype=torch.float32, device=dev)
+        ws = torch.empty(plan.workspace_bytes(), dtype=torch.uint8, device=dev)
+        sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+        coef = torch.zeros(1, dtype=torch.float32, device=dev)
+        Z.zero_reduce_shard(plan, slices.data_ptr(), ld, CODE["bf16"], 1.0, g.data_ptr(), ws.data_ptr(), True, st)
+        Z.zero_shard_norm(plan, ws.data_ptr(), 0.0, w.max_norm, flag.data_ptr(), sumsq.data_ptr(),
+                          coef.data_ptr(), st)
+        a = Z.adam_args(g_stash=g.data_ptr(), clip_coef=coef.data_ptr(), skip_in=flag.data_ptr(),
+                        **state_arg_dict(layout, A, A), **common)
+        Z.zero_adam_step(plan, a, st)
+        torch.cuda.synchronize()
+        c32 = F(coef.item())
+        res = OS.shard_step(sl, "bf16", "bf16", w.world, p_in, m_in, v_in, max_norm=w.max_norm,
+                            clip_override=c32, **kw)
+        assert np.array_equal(_take(g, idx_dev).view(np.uint32), res.g.view(np.uint32))
+        q = float(sumsq.item())
+        q_lib = float(sum(torch.sum(ch.double() ** 2).item() for ch in torch.split(g, 1 << 28)))
+        assert abs(q - q_lib) <= 1e-9 * q_lib, (q, q_lib)
+        out = A
+        del g, ws
+    else:
+        B = [torch.empty_like(A[0])]
+        a = Z.adam_args(grad=slices.data_ptr(), grad_ld=ld, grad_dtype=CODE["bf16"], overflow_out=flag.data_ptr(),
+                        **state_arg_dict(layout, A, B), **common)
+        Z.zero_adam_step(plan, a, st)
+        torch.cuda.synchronize()
+        res = OS.shard_step(sl, "bf16", "bf16", w.world, p_in, m_in, v_in, **kw)
+        out = B
+    assert int(flag.item()) == 0
+    say("  step done")
+    gp, gm, gv = (_take(out[0], soff_dev[i]) for i in range(3))
+    g_used = res.g if not clip else np.multiply(res.g, res.clip, dtype=F)
+    n, tot = compare_step(gp, gm, gv, res, p_in, m_in, v_in, g_used,
+                          OS.adam_consts(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.t0 + 1), "beyond int32")
+    assert n == tot, f"{tot - n} sampled state elements differ in the last bit"
+    check_params(_take(gather, gidx_dev), OC.narrow(gp, "bf16"), "bf16", "beyond int32 params")
+    goff = lay.segments[0][0]
+    sent = torch.tensor(SENTINEL["bf16"], dtype=torch.bfloat16, device=dev)
+    assert bool(torch.all(gather[:goff] == sent)) and bool(torch.all(gather[goff + S:] == sent))
+    del A, out, gather, slices
