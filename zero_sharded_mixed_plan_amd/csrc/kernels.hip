@@ -832,6 +832,15 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
   const int cnt = rest >= kVec ? kVec : (rest > 0 ? (int)rest : 0);
   float g[8];
   bool bad = false;
+  // the state goes out with the gradient loads: the step is latency bound, and
+  // only the stores wait for the skip decision
+  float p[8], m[8], v[8];
+  const int64_t o0 = state_off(a, j0);
+  if (cnt == kVec) {
+    ld8(a.p_in + o0, p);
+    ld8(a.m_in + o0, m);
+    ld8(a.v_in + o0, v);
+  }
   if (cnt == kVec) {
     float acc[8];
     if (a.grad_full)
@@ -863,15 +872,18 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
   }
   if (cnt == 0) return;
   if (any_bad) {
-    if (a.restore) copy_state(a, j0, cnt);
+    if (a.restore) {
+      if (cnt == kVec) {
+        st8(a.p_out + o0, p);
+        st8(a.m_out + o0, m);
+        st8(a.v_out + o0, v);
+      } else {
+        copy_state(a, j0, cnt);
+      }
+    }
     return;
   }
-  float p[8], m[8], v[8];
   if (cnt == kVec) {
-    const int64_t o0 = state_off(a, j0);
-    ld8(a.p_in + o0, p);
-    ld8(a.m_in + o0, m);
-    ld8(a.v_in + o0, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) adamw1(p[e], m[e], v[e], g[e], c);
     st8(a.p_out + o0, p);
