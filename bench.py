@@ -417,7 +417,7 @@ def main():
                          "launches) in this process, to scale HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one rank on one GPU; --gpus {args.gpus} is not "
+        print(f"bench.py measures one rank on one GPU; --gpus {args.gpus} is not "
               "supported (the multi-GPU collectives are out of scope)", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
