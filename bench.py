@@ -39,11 +39,38 @@ def round_up(x, m):
     return (x + m - 1) // m * m
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments, trailing blanks or empty lines (string and
+    character literals kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            while i < n and text[i] != "\n":
+                i += 1
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (line.rstrip() for line in "".join(out).splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def kernel_source_hash() -> str:
+    """Hash of the code (comments aside) of the kernels and their launch
+    configuration: profiles taken on other code are not reported as current."""
     h = hashlib.sha256()
     for f in ("kernels.hip", "abi.cpp", "zero_internal.h"):
-        with open(os.path.join(ROOT, "zero_sharded_mixed_plan_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "zero_sharded_mixed_plan_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -25,3 +25,15 @@ def test_resource_remarks_parsed_per_kernel():
 
 def test_the_resource_flag_is_part_of_the_build():
     assert "-Rpass-analysis=kernel-resource-usage" in B.FLAGS
+
+
+def test_profile_hash_ignores_comments_only():
+    """The source hash the benchmark compares with the committed profiles
+    covers code, not comments: a comment edit keeps the profiles current, a
+    code edit does not."""
+    import bench
+    code = 'int f(int x) {  // twice\n  /* the "sum" */ return x + x; // it\'s\n}\nconst char* s = "a // b";\n'
+    base = bench._code_only(code)
+    assert base == 'int f(int x) {\n   return x + x;\n}\nconst char* s = "a // b";'
+    assert bench._code_only(code.replace("twice", "double it")) == base
+    assert bench._code_only(code.replace("x + x", "x * 2")) != base

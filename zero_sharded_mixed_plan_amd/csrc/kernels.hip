@@ -2,11 +2,13 @@
 //
 // The step is a pure streaming update (well under one flop per byte), so it is
 // bound by HBM bandwidth, not by the matrix cores: every kernel here is written
-// for wide, coalesced global traffic.  Each thread owns kVec = 8 consecutive
-// elements, so every gradient slice is read with one 16-byte load (two for fp32)
-// and every fp32 state array with two 16-byte loads; a wave64 therefore touches
-// 1 KiB contiguous per 16-bit slice.  All loads of a tile are issued before the
-// arithmetic so enough bytes are in flight to cover HBM latency.
+// for wide, coalesced global traffic.  In the eight-element forms each thread
+// owns kVec = 8 consecutive elements, so every 16-bit gradient slice is read with
+// one 16-byte load (two for fp32) and every fp32 state array with two; a wave64
+// touches 1 KiB contiguous per 16-bit slice.  The narrow forms give a thread 4
+// elements and half the bytes in flight, which streams faster for most buffer
+// counts.  All loads of a tile are issued before the arithmetic so enough bytes
+// are in flight to cover HBM latency.
 //
 // What is computed follows zero_adam.py ("ZeRO 与 FSDP：切分优化器状态、梯度与参数",
 // section "从零实现 ZeRO 的 Adam"): SUM of the ranks' gradient pieces, / N, Adam on
@@ -661,7 +663,7 @@ __global__ __launch_bounds__(kThreads) void stash_step_kernel(const StepLaunch a
 }
 
 // ---------------------------------------------------------------------------
-// the fused update over few gradient buffers, four elements per lane
+// the narrow fused update: four elements per lane
 // ---------------------------------------------------------------------------
 
 // Four elements of a buffer, raw: 8 bytes for 16-bit types, 16 for fp32.
