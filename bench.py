@@ -180,6 +180,10 @@ def run(name, steps, warmup, with_cpu, copy_gbps=None):
         plan = Z.Plan.dim0([shape for _n, shape in w.tensors], w.world)
     else:
         plan = Z.Plan(W.numels(w.tensors), w.world, w.bucket_cap)
+    table = None
+    if plan.num_buckets > 192:   # as ZeroAdam does: the device piece table, one launch per step
+        table = torch.empty(plan.piece_table_bytes(), dtype=torch.uint8, device=dev)
+        plan.attach_piece_table(w.rank, table.data_ptr(), table.numel())
     S = plan.shard_numel
     lay = W.Layout(S=S, segments=plan.segments(w.rank), tensor_flat_off=plan.tensor_offsets())
     ld = round_up(S, 64)
@@ -356,6 +360,7 @@ def run(name, steps, warmup, with_cpu, copy_gbps=None):
                                                   "full": "one full all-reduced gradient (ZeRO-1)",
                                                   "reduce_only": "N slices, reduction pass alone"}[source],
             "plan_layout": {"flat": "flat buckets", "dim0": "per-parameter dim-0 (FSDP2)"}[plan_layout],
+            "piece_table": table is not None,
             "shard_elements": S, "world": w.world, "rank": w.rank,
             "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype, "buckets": plan.num_buckets,
             "clip": clip and not reduce_only, "state_layout": "tiled",

@@ -172,6 +172,32 @@ int64_t zero_state_numel(const zero_plan_t* plan, int32_t layout);
 size_t zero_workspace_bytes(const zero_plan_t* plan);
 
 /*
+ * Optional device piece table, for layouts with many gather pieces per rank
+ * (the dim-0 layout of a model with hundreds or thousands of parameters).
+ * Without it one launch of the update addresses at most 192 pieces (they
+ * travel as kernel arguments), so such a layout takes one launch per 192
+ * pieces, and zero_reduce_shard refuses a full-gradient layout with more
+ * than 192 pieces inside one 2048-element tile.
+ *
+ * zero_plan_piece_table_bytes: device bytes of one rank's table, 16 per
+ * piece (the plan's bucket count); 0 for a NULL plan.
+ *
+ * zero_plan_attach_piece_table: writes rank `rank`'s table into `table`
+ * (caller-owned device memory, 16-byte aligned, at least `bytes` =
+ * zero_plan_piece_table_bytes bytes; a synchronous copy from the host) and
+ * attaches it to the plan.  From then on zero_adam_step and zero_reduce_shard
+ * for that rank, on the device that was current at the attach, read the
+ * pieces from the table: one launch covers the whole shard.  Calls for
+ * another rank or device use the kernel-argument form.  The memory must stay
+ * allocated and unchanged until the plan is freed or another attach replaces
+ * it; table == NULL detaches.  Not thread-safe against concurrent calls that
+ * use the same plan.  Errors: ZERO_EINVAL (plan, rank, size), ZERO_EALIGN,
+ * ZERO_EHIP.
+ */
+int64_t zero_plan_piece_table_bytes(const zero_plan_t* plan);
+int zero_plan_attach_piece_table(zero_plan_t* plan, int32_t rank, void* table, int64_t bytes);
+
+/*
  * Where the gradient buffers a step reads come from.
  *
  * ZERO_GRAD_SHARD: each buffer is this rank's [S] shard, local index j.  With

@@ -126,7 +126,7 @@ class Rig:
     """Device buffers of one rank for workload w (inputs drawn on the CPU)."""
 
     def __init__(self, w: W.Workload, ld_align: int = 64, device="cuda", rank=None,
-                 layout: int = Z.ZERO_STATE_SEPARATE):
+                 layout: int = Z.ZERO_STATE_SEPARATE, table: bool = False):
         if rank is not None:
             import dataclasses
             w = dataclasses.replace(w, rank=rank)
@@ -134,6 +134,10 @@ class Rig:
         self.pl, self.lay = oracle_layout(w)
         self.S = self.lay.S
         self.plan = device_plan(w)
+        self.table = None
+        if table:   # the pieces from a device table: one launch for any number of pieces
+            self.table = torch.empty(self.plan.piece_table_bytes(), dtype=torch.uint8, device=device)
+            self.plan.attach_piece_table(w.rank, self.table.data_ptr(), self.table.numel())
         self.ld = round_up(self.S, ld_align)
         dev = torch.device(device)
         self.dev = dev

@@ -287,3 +287,19 @@ def test_stream_copy_validation(args, code):
     with pytest.raises(Z.ZeroError) as e:
         Z.zero_stream_copy(*args)
     assert e.value.code == code
+
+
+def test_piece_table_attach_validation():
+    """The piece table's size and the attach call's checks (no device memory is
+    touched: every case fails before the copy)."""
+    plan = Z.Plan.dim0([(256, 64), (256,), (10, 256), (10,)], 2)
+    assert plan.piece_table_bytes() == 16 * plan.num_buckets
+    for args, code in (((2, BASE, 64), Z.ZERO_EINVAL),       # rank out of range
+                       ((-1, BASE, 64), Z.ZERO_EINVAL),
+                       ((1, BASE + 8, 64), Z.ZERO_EALIGN),   # 16-byte alignment
+                       ((1, BASE, 63), Z.ZERO_EINVAL)):      # too small
+        with pytest.raises(Z.ZeroError) as e:
+            plan.attach_piece_table(*args)
+        assert e.value.code == code, Z.zero_last_error()
+    plan.attach_piece_table(0, 0, 0)                          # detaching needs no device
+    assert Z.lib().zero_plan_piece_table_bytes(None) == 0

@@ -168,11 +168,13 @@ def test_device_constants_match_host():
     assert not bad, bad[:5]
 
 
+@pytest.mark.parametrize("table", [False, True])
 @pytest.mark.parametrize("clip", [False, True])
-def test_sequence_many_pieces_dim0(clip):
-    """The FSDP2 dim-0 layout of a 20-layer model (more than 192 pieces per rank,
-    so the update runs in several launches and the last restore pass advances
-    the step control): five steps with an overflow, against the oracle."""
+def test_sequence_many_pieces_dim0(clip, table):
+    """The FSDP2 dim-0 layout of a 20-layer model (more than 192 pieces per rank:
+    without the piece table the update runs in several launches and the last
+    restore pass advances the step control; with it, in one): five steps with
+    an overflow, against the oracle."""
     w = W.Workload(name="dim0_many", tensors=tuple(W.gpt2(n_layer=20, d=64, vocab=503, n_ctx=96)), world=8,
                    rank=5, bucket_cap=0, grad_dtype="f16", param_dtype="f16", lr=1e-3, weight_decay=0.05,
                    loss_scale=512.0, steps=5, seed=17, plan_layout="dim0", inject_inf_step=2,
@@ -184,8 +186,8 @@ def test_sequence_many_pieces_dim0(clip):
     opt = ZeroAdam([s for _n, s in w.tensors], w.world, w.rank, lr=w.lr, weight_decay=w.weight_decay,
                    grad_dtype=torch.float16, param_dtype=torch.float16, max_norm=w.max_norm,
                    loss_scale=w.loss_scale, dynamic_loss_scale=True, growth_interval=2, master=master.cuda(),
-                   layout="dim0", device_control=True)
-    say(f"device control dim0 S={S} pieces={len(lay.segments)} clip={clip}")
+                   layout="dim0", device_control=True, piece_table=table)
+    say(f"device control dim0 S={S} pieces={len(lay.segments)} clip={clip} table={table}")
     p, m, v = master.numpy(), m0.numpy(), v0.numpy()
     t = 0
     sc = ORS.ScalerState(scale=F32(w.loss_scale), growth_tracker=0, growth_interval=2)

@@ -53,13 +53,13 @@ def _grads(rig: Rig, source: str, step: int):
     return full.to(rig.dev), dict(count=count, layout=Z.ZERO_GRAD_FULL, ld=ldf), sl
 
 
-def run_workload(w: W.Workload, ld_align=64, rank=None, steps=None, layout=SEP, source="slices"):
+def run_workload(w: W.Workload, ld_align=64, rank=None, steps=None, layout=SEP, source="slices", table=False):
     """Run w.steps steps on the GPU and in the oracle; compare everything."""
-    rig = Rig(w, ld_align=ld_align, rank=rank, layout=layout)
+    rig = Rig(w, ld_align=ld_align, rank=rank, layout=layout, table=table)
     w = rig.w
     say(f"workload {w.name} S={rig.S} N={w.world} rank={w.rank} grads={w.grad_dtype} "
         f"params={w.param_dtype} buckets={len(rig.lay.segments)} ld={rig.ld} layout={layout} "
-        f"source={source}")
+        f"source={source} table={table}")
     p, m, v = rig.p0, rig.m0, rig.v0
     gather_ref = rig.gather0.copy()
     cur, nxt = rig.A, rig.B
@@ -466,3 +466,30 @@ def test_full_gradient_clipped(case):
     w = dataclasses.replace(w, max_norm=0.02)
     for layout in (SEP, TILED):
         run_workload(w, layout=layout, source="full")
+
+
+# ---------------------------------------------------------------------------
+# the device piece table: one launch for any number of pieces
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("source", ["slices", "stored", "full"])
+@pytest.mark.parametrize("clip", [False, True])
+def test_piece_table_many_pieces(source, clip):
+    """A dim-0 layout of 244 pieces per rank with the piece table attached: the
+    whole shard in one launch, equal to the oracle (the same layout without
+    the table takes two launches, covered above)."""
+    w = _dim0(W.gpt2(n_layer=20, d=64, vocab=503, n_ctx=96), 8, 5, "bf16", "bf16",
+              max_norm=(0.02 if clip else 0.0))
+    for layout in (SEP, TILED):
+        run_workload(w, layout=layout, source=source, table=True)
+
+
+@pytest.mark.parametrize("source", ["full", "full_n"])
+def test_piece_table_lifts_the_tile_limit(source):
+    """300 one-element parameters and a large one on 2 ranks: the first
+    2048-element tile holds more than 192 pieces, which the full-gradient
+    reduction refuses without the table and serves with it."""
+    tm = [(f"s{i}", (1,)) for i in range(300)] + [("big", (5000,))]
+    w = _dim0(tm, 2, 1, "f32", "f32", max_norm=0.5)
+    run_workload(w, layout=TILED, source=source, table=True)
+    run_workload(dataclasses.replace(w, max_norm=0.0), layout=TILED, source=source, table=True)

@@ -27,7 +27,8 @@ EXPORTS = [
     "zero_plan", "zero_plan_dim0", "zero_plan_free", "zero_plan_shard_numel", "zero_plan_total_numel",
     "zero_plan_padded_numel", "zero_plan_world", "zero_plan_num_buckets", "zero_plan_num_tensors",
     "zero_plan_bucket", "zero_plan_tensor", "zero_plan_rank_segment", "zero_plan_bytes",
-    "zero_state_numel", "zero_workspace_bytes", "zero_reduce_shard", "zero_shard_norm", "zero_adam_step",
+    "zero_state_numel", "zero_workspace_bytes", "zero_plan_piece_table_bytes", "zero_plan_attach_piece_table",
+    "zero_reduce_shard", "zero_shard_norm", "zero_adam_step",
     "zero_scaler_init", "zero_scaler_update", "zero_scaler_inv_scale", "zero_plan_hash",
     "zero_checkpoint_save", "zero_checkpoint_load", "zero_stream_copy", "zero_last_error", "zero_version",
 ]
@@ -138,6 +139,8 @@ def load(path: str, required: bool = True) -> ctypes.CDLL:
         "zero_plan_bytes": (ctypes.c_int, [vp, i32, ctypes.POINTER(f64), P64]),
         "zero_state_numel": (i64, [vp, i32]),
         "zero_workspace_bytes": (ctypes.c_size_t, [vp]),
+        "zero_plan_piece_table_bytes": (i64, [vp]),
+        "zero_plan_attach_piece_table": (ctypes.c_int, [vp, i32, vp, i64]),
         "zero_reduce_shard": (ctypes.c_int, [vp, i32, vp, i64, i32, i32, ctypes.c_int, f32, vp, vp, i32, vp, vp]),
         "zero_shard_norm": (ctypes.c_int, [vp, vp, f64, f64, vp, vp, vp, vp]),
         "zero_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(zero_adam_args_t), vp]),
@@ -279,6 +282,15 @@ class Plan:
         f, p = ctypes.c_double(), ctypes.c_int64()
         _check(lib().zero_plan_bytes(self.handle, stage, ctypes.byref(f), ctypes.byref(p)))
         return f.value, p.value
+
+    def piece_table_bytes(self) -> int:
+        """Device bytes of one rank's piece table (16 per piece)."""
+        return lib().zero_plan_piece_table_bytes(self.handle)
+
+    def attach_piece_table(self, rank: int, table: int, nbytes: int) -> None:
+        """Write rank's piece table into device memory `table` and attach it
+        (one launch per step for any number of pieces); table=0 detaches."""
+        _check(lib().zero_plan_attach_piece_table(self.handle, int(rank), table or None, int(nbytes)))
 
     def workspace_bytes(self) -> int:
         return lib().zero_workspace_bytes(self.handle)

@@ -78,6 +78,15 @@ int64_t grad_span(int64_t ld, int32_t count, int64_t len, int gb) {
   return ((int64_t)(count - 1) * ld + len) * gb;
 }
 
+// The plan's attached device piece table if it serves `rank` on the current
+// device, else NULL.
+const zk::Seg* piece_table_for(const zero_plan_t* plan, int32_t rank) {
+  if (plan->table == nullptr || plan->table_rank != rank) return nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != plan->table_device) return nullptr;
+  return static_cast<const zk::Seg*>(plan->table);
+}
+
 // device address of ctl->k (address arithmetic only; ctl is device memory)
 const float* ctl_consts(const zero_step_ctl_t* ctl) {
   return reinterpret_cast<const float*>(reinterpret_cast<const char*>(ctl) + offsetof(zero_step_ctl_t, k));
@@ -140,10 +149,18 @@ extern "C" int zero_reduce_shard(const zero_plan_t* plan, int32_t rank, const vo
     if (ctl && (rc = zk::launch_ctl_begin(ctl, 0, 0.0, 0.0, 0.0, nullptr, stream))) return rc;
     return zk::launch_reduce(a, grad_dtype, nblocks, stream);
   }
-  // Full-gradient layout: launches over runs of whole tiles whose elements lie in
-  // at most kMaxSeg pieces (each workgroup still writes its own partial).
+  // Full-gradient layout: with the device piece table one launch over every
+  // tile; else launches over runs of whole tiles whose elements lie in at most
+  // kMaxSeg pieces (each workgroup still writes its own partial).
   const auto& B = plan->buckets;
   const int nb = (int)B.size();
+  if (const zk::Seg* table = piece_table_for(plan, rank)) {
+    a.blk0 = 0;
+    a.nseg = nb;
+    a.table = table;
+    if (ctl && (rc = zk::launch_ctl_begin(ctl, 0, 0.0, 0.0, 0.0, nullptr, stream))) return rc;
+    return zk::launch_reduce(a, grad_dtype, nblocks, stream);
+  }
   auto first_piece = [&](int64_t j) {  // first piece whose local end is past element j
     int lo = 0, hi = nb - 1;
     while (lo < hi) {
@@ -372,7 +389,10 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
   struct Group { int64_t v_lo, v_hi; int first, count; };
   std::vector<Group> groups;
   const int64_t nvec = (S + zk::kVec - 1) / zk::kVec;
-  {
+  const zk::Seg* table = piece_table_for(plan, A.rank);
+  if (table) {  // every piece in one launch, read from the device table
+    groups.push_back(Group{0, nvec, 0, nb});
+  } else {
     int first = 0;
     int64_t v_lo = 0;
     while (first < nb) {
@@ -392,17 +412,24 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
     }
   }
 
-  int rc = ZERO_OK;
-  if (!stash && S <= zk::kSmallShard && groups.size() == 1) {
-    // one workgroup decides the skip before writing: a single launch
-    L.v_lo = 0;
-    L.v_hi = nvec;
-    L.nseg = groups[0].count;
-    for (int s = 0; s < L.nseg; ++s) {
-      const auto& B = plan->buckets[groups[0].first + s];
+  // one launch's vector range and pieces: kernel arguments, or the table
+  auto set_group = [&](const Group& g) {
+    L.v_lo = g.v_lo;
+    L.v_hi = g.v_hi;
+    L.nseg = g.count;
+    L.table = table;
+    if (table) return;
+    for (int s = 0; s < g.count; ++s) {
+      const auto& B = plan->buckets[g.first + s];
       L.seg[s].end = B.local_off + B.shard;
       L.seg[s].delta = (B.base + (int64_t)A.rank * B.shard) - B.local_off;
     }
+  };
+
+  int rc = ZERO_OK;
+  if (!stash && S <= zk::kSmallShard && groups.size() == 1) {
+    // one workgroup decides the skip before writing: a single launch
+    set_group(groups[0]);
     // the workgroup derives the step control's constants and advances it itself
     L.kdev = nullptr;
     L.ctl = ctl;
@@ -420,14 +447,7 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
   rc = zk::record_event(A.ev_begin, stream);
   if (rc) return rc;
   for (const Group& g : groups) {
-    L.v_lo = g.v_lo;
-    L.v_hi = g.v_hi;
-    L.nseg = g.count;
-    for (int s = 0; s < g.count; ++s) {
-      const auto& B = plan->buckets[g.first + s];
-      L.seg[s].end = B.local_off + B.shard;
-      L.seg[s].delta = (B.base + (int64_t)A.rank * B.shard) - B.local_off;
-    }
+    set_group(g);
     rc = zk::launch_step(L, A.grad_dtype, A.param_dtype, stash, stream);
     if (rc) return rc;
   }
@@ -436,20 +456,47 @@ extern "C" int zero_adam_step(const zero_plan_t* plan, const zero_adam_args_t* a
   if (strict) {
     for (const Group& g : groups) {
       L.ctl = (&g == &groups.back()) ? ctl : nullptr;  // the last restore pass advances the step control
-      L.v_lo = g.v_lo;
-      L.v_hi = g.v_hi;
-      L.nseg = g.count;
-      for (int s = 0; s < g.count; ++s) {
-        const auto& B = plan->buckets[g.first + s];
-        L.seg[s].end = B.local_off + B.shard;
-        L.seg[s].delta = (B.base + (int64_t)A.rank * B.shard) - B.local_off;
-      }
+      set_group(g);
       rc = zk::launch_recast(L, A.param_dtype, A.overflow_out, stream);
       if (rc) return rc;
     }
   }
   // the fused step advanced the step control in its restore pass
   if (ctl && stash) return zk::launch_ctl_end(ctl, A.skip_in, stream);
+  return ZERO_OK;
+}
+
+extern "C" int64_t zero_plan_piece_table_bytes(const zero_plan_t* plan) {
+  return plan ? (int64_t)plan->buckets.size() * (int64_t)sizeof(zk::Seg) : 0;
+}
+
+extern "C" int zero_plan_attach_piece_table(zero_plan_t* plan, int32_t rank, void* table, int64_t bytes) {
+  if (!plan) return fail(ZERO_EINVAL, "zero_plan_attach_piece_table: plan is NULL");
+  if (!table) {  // detach
+    plan->table = nullptr;
+    plan->table_rank = -1;
+    plan->table_device = -1;
+    return ZERO_OK;
+  }
+  if (rank < 0 || rank >= plan->world) return fail(ZERO_EINVAL, "zero_plan_attach_piece_table: rank out of range");
+  const int64_t need = zero_plan_piece_table_bytes(plan);
+  if (bytes < need)
+    return fail(ZERO_EINVAL, "zero_plan_attach_piece_table: the table needs " + std::to_string(need) + " bytes");
+  if (!aligned(table, 16)) return fail(ZERO_EALIGN, "zero_plan_attach_piece_table: table must be 16-byte aligned");
+  std::vector<zk::Seg> host(plan->buckets.size());
+  for (size_t b = 0; b < host.size(); ++b) {
+    const auto& B = plan->buckets[b];
+    host[b].end = B.local_off + B.shard;
+    host[b].delta = (B.base + (int64_t)rank * B.shard) - B.local_off;
+  }
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipMemcpy(table, host.data(), (size_t)need, hipMemcpyHostToDevice);
+  if (e != hipSuccess)
+    return fail(ZERO_EHIP, std::string("zero_plan_attach_piece_table: ") + hipGetErrorString(e));
+  plan->table = table;
+  plan->table_rank = rank;
+  plan->table_device = dev;
   return ZERO_OK;
 }
 

@@ -401,6 +401,20 @@ struct SegRange {
   int s0, s1;  // pieces s0 .. s1
 };
 
+// Piece i of the launch: from the kernel arguments, or from the device table
+// attached to the plan (read through the constant address space: no kernel
+// writes it, so the reads are scalar loads like those of the arguments).
+typedef const __attribute__((address_space(4))) Seg* ConstSegs;
+
+template <class LA>
+__device__ __forceinline__ int64_t seg_end(const LA& a, int i) {
+  return a.table != nullptr ? ((ConstSegs)a.table)[i].end : a.seg[i].end;
+}
+template <class LA>
+__device__ __forceinline__ int64_t seg_delta(const LA& a, int i) {
+  return a.table != nullptr ? ((ConstSegs)a.table)[i].delta : a.seg[i].delta;
+}
+
 template <class LA>
 __device__ __forceinline__ SegRange wave_segs(const LA& a, int64_t lo, int64_t hi) {
   // a few pieces: scan them all (no chain of dependent argument loads)
@@ -408,13 +422,13 @@ __device__ __forceinline__ SegRange wave_segs(const LA& a, int64_t lo, int64_t h
   int L = 0, R = a.nseg - 1;
   while (L < R) {  // first piece ending after lo
     const int M = (L + R) >> 1;
-    if (a.seg[M].end > lo) R = M; else L = M + 1;
+    if (seg_end(a, M) > lo) R = M; else L = M + 1;
   }
   const int s0 = L;
   R = a.nseg - 1;
   while (L < R) {  // first piece reaching hi
     const int M = (L + R) >> 1;
-    if (a.seg[M].end >= hi) R = M; else L = M + 1;
+    if (seg_end(a, M) >= hi) R = M; else L = M + 1;
   }
   return SegRange{s0, L};
 }
@@ -429,9 +443,9 @@ __device__ __forceinline__ SegRange wave_segs_v(const LA& a, int64_t v) {
 // gather index offset of local element j, j inside the wave's pieces
 template <class LA>
 __device__ __forceinline__ int64_t delta_of(const LA& a, const SegRange& r, int64_t j) {
-  int64_t d = a.seg[r.s0].delta;
+  int64_t d = seg_delta(a, r.s0);
   for (int s = r.s0; s < r.s1; ++s)
-    if (j >= a.seg[s].end) d = a.seg[s + 1].delta;
+    if (j >= seg_end(a, s)) d = seg_delta(a, s + 1);
   return d;
 }
 

@@ -21,6 +21,10 @@ struct zero_plan {
   std::vector<Bucket> buckets;
   std::vector<int32_t> tensor_bucket;
   std::vector<int64_t> tensor_offset;
+  // optional device piece table (zero_plan_attach_piece_table)
+  const void* table = nullptr;
+  int32_t table_rank = -1;
+  int32_t table_device = -1;
 };
 
 namespace zk {
@@ -93,6 +97,7 @@ struct StepLaunch {
   int64_t S;              // shard length (elements at or past S do not exist)
   int64_t v_lo, v_hi;     // vectors [v_lo, v_hi) of kVec elements
   int32_t nseg;
+  const Seg* table;       // non-null: the pieces are read from this device table, seg[] is unused
   Seg seg[kMaxSeg];
 };
 
@@ -115,6 +120,7 @@ struct ReduceLaunch {
   int64_t nvec;           // ceil(S / kVec)
   int64_t blk0;           // first tile (workgroup) of this launch
   int32_t nseg;           // pieces of this launch's tiles (full-gradient layout)
+  const Seg* table;       // non-null: the pieces are read from this device table
   Seg seg[kMaxSeg];
 };
 

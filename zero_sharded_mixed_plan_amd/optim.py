@@ -114,6 +114,10 @@ class ZeroAdam:
     (it returns None), a skipped step leaves the output state current, and the
     step can be captured in a HIP graph and replayed for every step.  t,
     skipped and loss_scale read the device copy (a wait).
+
+    piece_table: attach the rank's piece table in device memory (default: when
+    the layout has more than 192 pieces, the most one launch addresses from its
+    kernel arguments).
     """
 
     def __init__(self, numels: Sequence, world: int, rank: int, *, lr: float,
@@ -123,7 +127,7 @@ class ZeroAdam:
                  growth_interval: int = 2000, master: Optional[torch.Tensor] = None,
                  gather: Optional[torch.Tensor] = None, device="cuda",
                  state_layout: int = _abi.ZERO_STATE_TILED, layout: str = "flat",
-                 device_control: bool = False):
+                 device_control: bool = False, piece_table: Optional[bool] = None):
         if layout == "dim0":
             self.plan = _abi.Plan.dim0(numels, world)
         elif layout == "flat":
@@ -157,6 +161,12 @@ class ZeroAdam:
                 self._state[0][0].copy_(pack_state(master.to(**f32), z, z, self._state[0][0].numel()))
             else:
                 self._state[0][0].copy_(master)
+        # many pieces (a dim-0 layout of a large model): the piece table in device
+        # memory, so each step is one launch rather than one per 192 pieces
+        self._table = None
+        if piece_table or (piece_table is None and self.plan.num_buckets > 192):
+            self._table = torch.empty(self.plan.piece_table_bytes(), dtype=torch.uint8, device=dev)
+            self.plan.attach_piece_table(self.rank, self._table.data_ptr(), self._table.numel())
         self.gather = gather if gather is not None else torch.zeros(
             self.plan.padded_numel, dtype=param_dtype, device=dev)
         if self.gather.numel() != self.plan.padded_numel or self.gather.dtype != param_dtype:
