@@ -237,7 +237,9 @@ typedef struct zero_step_ctl zero_step_ctl_t;
  * ZERO_GRAD_FULL: whole flat gradients of zero_plan_padded_numel elements, read
  * at rank `rank`'s gather offsets (ZeRO-1), element aligned; the work is then
  * split into launches over runs of 2048-element tiles that touch at most 192
- * pieces, and a layout with more pieces inside one tile is refused.  `rank`
+ * pieces, and a layout with more pieces inside one tile is refused -- unless
+ * the rank's piece table is attached (zero_plan_attach_piece_table), which
+ * makes it one launch for any layout.  `rank`
  * is used by the full layout only.  If g_out != NULL, g is stored there (fp32,
  * [S], 16-byte aligned).  Per 2048-element tile, an overflow word (any
  * non-finite g) and, if want_sumsq, the float64 sum of g^2 go to `ws`
