@@ -437,6 +437,55 @@ def copy_probe(steps, warmup, gib=4.0):
     print(json.dumps(out), flush=True)
 
 
+def checkpoint_probe(name=DEFAULT, reps=2):
+    """Sharded checkpoint of one rank's optimizer state (master, m, v in the
+    tiled device layout; 12 B per shard element on disk plus a 128-byte header):
+    save and load through the library, timed on the host clock, bytes of the
+    file per second.  The loaded state must equal the saved one bit for bit."""
+    import tempfile
+
+    import torch
+
+    import workloads as W
+    import zero_sharded_mixed_plan_amd as Z
+    from zero_sharded_mixed_plan_amd.optim import pack_state
+
+    w = W.FULL[name]
+    plan = Z.Plan(W.numels(w.tensors), w.world, w.bucket_cap)
+    S = plan.shard_numel
+    lay = W.Layout(S=S, segments=plan.segments(w.rank), tensor_flat_off=plan.tensor_offsets())
+    p0, m0, v0 = W.make_state(w, lay, "cuda")
+    A = pack_state(p0, m0, v0, plan.state_numel(Z.ZERO_STATE_TILED))
+    del p0, m0, v0
+    B = torch.full_like(A, float("nan"))
+    sc = Z.Scaler(init_scale=w.loss_scale)
+    st = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    nbytes = 12 * S + 128
+    save_s, load_s = [], []
+    with tempfile.TemporaryDirectory(dir=os.environ.get("TMPDIR", "/tmp")) as d:
+        path = os.path.join(d, f"rank{w.rank}.zshard")
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            Z.zero_checkpoint_save(plan, w.rank, path, Z.ZERO_STATE_TILED, A.data_ptr(), 0, 0,
+                                   w.t0, sc.s, st)
+            save_s.append(time.perf_counter() - t0)
+            if os.path.getsize(path) != nbytes:
+                raise RuntimeError("checkpoint file has the wrong size")
+            t0 = time.perf_counter()
+            meta = Z.zero_checkpoint_load(plan, w.rank, path, Z.ZERO_STATE_TILED, B.data_ptr(), 0, 0, st)
+            load_s.append(time.perf_counter() - t0)
+            if int(meta.step) != w.t0 or not torch.equal(A.view(torch.int32), B.view(torch.int32)):
+                raise RuntimeError("loaded state differs from the saved state")
+    out = {"metric": "sharded checkpoint of one rank's optimizer state (save / load)",
+           "workload": name, "shard_elements": S, "file_bytes": nbytes,
+           "save_s": min(save_s), "load_s": min(load_s),
+           "save_GBps": nbytes / min(save_s) / 1e9, "load_GBps": nbytes / min(load_s) / 1e9,
+           "note": "host clock; device -> pinned staging -> file (page cache), FNV-1a checksums; "
+                   "the loaded state is compared with the saved one bit for bit"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,6 +495,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline")
     ap.add_argument("--report", default=None, help="append every workload's JSON line here")
     ap.add_argument("--copy-probe", action="store_true", help="time a plain copy kernel only")
+    ap.add_argument("--checkpoint", action="store_true",
+                    help="time a sharded checkpoint save and load of the default workload's state")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="first run a plain copy of known size (torch.neg over 2^28 fp32, 3 "
                          "launches) in this process, to scale HBM byte counters")
@@ -456,6 +507,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.steps, args.warmup)
+        return
+    if args.checkpoint:
+        checkpoint_probe()
         return
     if args.copy_calibrate:
         import torch

@@ -75,6 +75,24 @@ inline uint64_t fnv(uint64_t h, const void* p, size_t n) {
   return h;
 }
 
+// FNV-1a of three byte strings of equal length at once: the same three
+// results as three separate passes, with three independent multiply chains in
+// flight (the byte-serial hash is latency bound, about 1 GB/s per chain).
+inline void fnv3(uint64_t h[3], const void* p0, const void* p1, const void* p2, size_t n) {
+  const unsigned char* a = static_cast<const unsigned char*>(p0);
+  const unsigned char* b = static_cast<const unsigned char*>(p1);
+  const unsigned char* c = static_cast<const unsigned char*>(p2);
+  uint64_t x = h[0], y = h[1], z = h[2];
+  for (size_t i = 0; i < n; ++i) {
+    x = (x ^ a[i]) * kFnvPrime;
+    y = (y ^ b[i]) * kFnvPrime;
+    z = (z ^ c[i]) * kFnvPrime;
+  }
+  h[0] = x;
+  h[1] = y;
+  h[2] = z;
+}
+
 inline uint64_t fnv_i64(uint64_t h, int64_t x) {
   unsigned char b[8];
   for (int i = 0; i < 8; ++i) b[i] = (unsigned char)((uint64_t)x >> (8 * i));  // little-endian bytes
@@ -106,7 +124,7 @@ namespace {
 
 constexpr size_t kHeader = 128;
 constexpr uint32_t kVersion = 1;
-constexpr int64_t kChunk = int64_t(1) << 22;  // elements per staging chunk (a multiple of the state tile)
+constexpr int64_t kChunk = int64_t(1) << 21;  // elements per staging chunk (a multiple of the state tile)
 static_assert(kChunk % zk::kStateTile == 0, "chunks hold whole tiles");
 
 void put_u32(unsigned char* h, size_t off, uint32_t x) {
@@ -141,15 +159,31 @@ int hip_fail(const char* fn, const char* what, hipError_t e) {
   return fail(ZERO_EHIP, std::string(fn) + ": " + what + ": " + hipGetErrorString(e));
 }
 
-// pinned host staging for master, m, v of one chunk, plus the tiled form
+// Pinned host staging: two sets, each master, m, v of one chunk plus their
+// tiled form.  Chunk c uses set c % 2, so the copy of one chunk runs while the
+// host hashes and writes (or reads and hashes) the other; an event per set
+// marks when its copy has finished.  Destruction waits for the stream, so no
+// copy is still in flight into or out of freed memory on an error return.
 struct Staging {
-  float* buf = nullptr;  // 3 * kChunk floats (separate) followed by 3 * kChunk (tiled)
+  float* buf = nullptr;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  hipStream_t st = nullptr;
   ~Staging() {
+    if (buf) (void)hipStreamSynchronize(st);
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
     if (buf) (void)hipHostFree(buf);
   }
-  hipError_t alloc() { return hipHostMalloc((void**)&buf, 6 * (size_t)kChunk * sizeof(float), 0); }
-  float* arr(int k) { return buf + (size_t)k * kChunk; }
-  float* tiles() { return buf + 3 * (size_t)kChunk; }
+  hipError_t alloc(hipStream_t s) {
+    st = s;
+    for (hipEvent_t& e : ev) {
+      const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+      if (r != hipSuccess) return r;
+    }
+    return hipHostMalloc((void**)&buf, 12 * (size_t)kChunk * sizeof(float), 0);
+  }
+  float* arr(int set, int k) { return buf + (size_t)(set * 6 + k) * kChunk; }
+  float* tiles(int set) { return buf + (size_t)(set * 6 + 3) * kChunk; }
 };
 
 struct File {
@@ -201,7 +235,7 @@ extern "C" int zero_checkpoint_save(const zero_plan_t* plan, int32_t rank, const
   hipStream_t st = (hipStream_t)stream;
 
   Staging stg;
-  if (stg.alloc() != hipSuccess || !stg.buf) return fail(ZERO_ENOMEM, std::string(fn) + ": pinned staging");
+  if (stg.alloc(st) != hipSuccess || !stg.buf) return fail(ZERO_ENOMEM, std::string(fn) + ": pinned staging");
   const std::string tmp = std::string(path) + ".tmp";
   File out;
   out.f = std::fopen(tmp.c_str(), "wb");
@@ -209,33 +243,48 @@ extern "C" int zero_checkpoint_save(const zero_plan_t* plan, int32_t rank, const
   unsigned char h[kHeader] = {};
   if (std::fwrite(h, 1, kHeader, out.f) != kHeader) return fail(ZERO_EIO, std::string(fn) + ": write failed");
 
-  // payload: master, m, v regions; chunks of kChunk elements of all three at once
+  // payload: master, m, v regions; chunks of kChunk elements of all three at
+  // once, the copy of chunk c + 1 in flight while chunk c is hashed and written
   uint64_t sum[3] = {kFnvOffset, kFnvOffset, kFnvOffset};
   const float* src[3] = {master, m, v};
-  for (int64_t j0 = 0; j0 < S; j0 += kChunk) {
-    const int64_t n = (S - j0 < kChunk) ? S - j0 : kChunk;
+  const int64_t nchunks = (S + kChunk - 1) / kChunk;
+  auto issue = [&](int64_t c) -> hipError_t {  // chunk c: device -> staging set c % 2
+    const int set = (int)(c & 1);
+    const int64_t j0 = c * kChunk, n = (S - j0 < kChunk) ? S - j0 : kChunk;
     hipError_t e = hipSuccess;
     if (tiled) {
       const int64_t t0 = j0 / zk::kStateTile, nt = (n + zk::kStateTile - 1) / zk::kStateTile;
-      e = hipMemcpyAsync(stg.tiles(), master + t0 * 3 * zk::kStateTile,
+      e = hipMemcpyAsync(stg.tiles(set), master + t0 * 3 * zk::kStateTile,
                          (size_t)nt * 3 * zk::kStateTile * sizeof(float), hipMemcpyDeviceToHost, st);
-      if (e == hipSuccess) e = hipStreamSynchronize(st);
-      if (e != hipSuccess) return hip_fail(fn, "copy to host", e);
-      for (int64_t i = 0; i < n; ++i) {
-        const int64_t t = i / zk::kStateTile, r = i % zk::kStateTile;
-        for (int k = 0; k < 3; ++k) stg.arr(k)[i] = stg.tiles()[(t * 3 + k) * zk::kStateTile + r];
-      }
     } else {
       for (int k = 0; k < 3 && e == hipSuccess; ++k)
-        e = hipMemcpyAsync(stg.arr(k), src[k] + j0, (size_t)n * sizeof(float), hipMemcpyDeviceToHost, st);
-      if (e == hipSuccess) e = hipStreamSynchronize(st);
-      if (e != hipSuccess) return hip_fail(fn, "copy to host", e);
+        e = hipMemcpyAsync(stg.arr(set, k), src[k] + j0, (size_t)n * sizeof(float), hipMemcpyDeviceToHost, st);
     }
+    return e == hipSuccess ? hipEventRecord(stg.ev[set], st) : e;
+  };
+  if (nchunks > 0) {
+    const hipError_t e = issue(0);
+    if (e != hipSuccess) return hip_fail(fn, "copy to host", e);
+  }
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int set = (int)(c & 1);
+    const int64_t j0 = c * kChunk, n = (S - j0 < kChunk) ? S - j0 : kChunk;
+    // set (c + 1) % 2 was last used by chunk c - 1, which is written already
+    hipError_t e = c + 1 < nchunks ? issue(c + 1) : hipSuccess;
+    if (e == hipSuccess) e = hipEventSynchronize(stg.ev[set]);
+    if (e != hipSuccess) return hip_fail(fn, "copy to host", e);
+    if (tiled) {
+      const float* tb = stg.tiles(set);
+      for (int64_t i = 0; i < n; ++i) {
+        const int64_t t = i / zk::kStateTile, r = i % zk::kStateTile;
+        for (int k = 0; k < 3; ++k) stg.arr(set, k)[i] = tb[(t * 3 + k) * zk::kStateTile + r];
+      }
+    }
+    fnv3(sum, stg.arr(set, 0), stg.arr(set, 1), stg.arr(set, 2), (size_t)n * sizeof(float));
     for (int k = 0; k < 3; ++k) {
-      sum[k] = fnv(sum[k], stg.arr(k), (size_t)n * sizeof(float));
       const long long off = (long long)kHeader + ((long long)k * S + j0) * (long long)sizeof(float);
       if (fseeko(out.f, (off_t)off, SEEK_SET) != 0 ||
-          std::fwrite(stg.arr(k), sizeof(float), (size_t)n, out.f) != (size_t)n)
+          std::fwrite(stg.arr(set, k), sizeof(float), (size_t)n, out.f) != (size_t)n)
         return fail(ZERO_EIO, std::string(fn) + ": write failed (" + tmp + ")");
     }
   }
@@ -300,36 +349,46 @@ extern "C" int zero_checkpoint_load(const zero_plan_t* plan, int32_t rank, const
     return fail(ZERO_EIO, std::string(fn) + ": file size does not match the shard");
 
   Staging stg;
-  if (stg.alloc() != hipSuccess || !stg.buf) return fail(ZERO_ENOMEM, std::string(fn) + ": pinned staging");
+  if (stg.alloc(st) != hipSuccess || !stg.buf) return fail(ZERO_ENOMEM, std::string(fn) + ": pinned staging");
   uint64_t sum[3] = {kFnvOffset, kFnvOffset, kFnvOffset};
   float* dst[3] = {master, m, v};
-  for (int64_t j0 = 0; j0 < S; j0 += kChunk) {
-    const int64_t n = (S - j0 < kChunk) ? S - j0 : kChunk;
+  const int64_t nchunks = (S + kChunk - 1) / kChunk;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int set = (int)(c & 1);
+    const int64_t j0 = c * kChunk, n = (S - j0 < kChunk) ? S - j0 : kChunk;
+    // this set's staging was last used by the copy of chunk c - 2: wait for it
+    if (c >= 2) {
+      const hipError_t e = hipEventSynchronize(stg.ev[set]);
+      if (e != hipSuccess) return hip_fail(fn, "copy to device", e);
+    }
     for (int k = 0; k < 3; ++k) {
       const long long off = (long long)kHeader + ((long long)k * S + j0) * (long long)sizeof(float);
       if (fseeko(in.f, (off_t)off, SEEK_SET) != 0 ||
-          std::fread(stg.arr(k), sizeof(float), (size_t)n, in.f) != (size_t)n)
+          std::fread(stg.arr(set, k), sizeof(float), (size_t)n, in.f) != (size_t)n)
         return fail(ZERO_EIO, std::string(fn) + ": read failed");
-      sum[k] = fnv(sum[k], stg.arr(k), (size_t)n * sizeof(float));
     }
+    fnv3(sum, stg.arr(set, 0), stg.arr(set, 1), stg.arr(set, 2), (size_t)n * sizeof(float));
     hipError_t e = hipSuccess;
     if (tiled) {
       const int64_t t0 = j0 / zk::kStateTile, nt = (n + zk::kStateTile - 1) / zk::kStateTile;
-      float* tb = stg.tiles();
+      float* tb = stg.tiles(set);
       for (int64_t t = 0; t < nt; ++t)
         for (int k = 0; k < 3; ++k)
           for (int64_t r = 0; r < zk::kStateTile; ++r) {
             const int64_t i = t * zk::kStateTile + r;
-            tb[(t * 3 + k) * zk::kStateTile + r] = i < n ? stg.arr(k)[i] : 0.0f;  // past S: zeros
+            tb[(t * 3 + k) * zk::kStateTile + r] = i < n ? stg.arr(set, k)[i] : 0.0f;  // past S: zeros
           }
       e = hipMemcpyAsync(master + t0 * 3 * zk::kStateTile, tb, (size_t)nt * 3 * zk::kStateTile * sizeof(float),
                          hipMemcpyHostToDevice, st);
     } else {
       for (int k = 0; k < 3 && e == hipSuccess; ++k)
-        e = hipMemcpyAsync(dst[k] + j0, stg.arr(k), (size_t)n * sizeof(float), hipMemcpyHostToDevice, st);
+        e = hipMemcpyAsync(dst[k] + j0, stg.arr(set, k), (size_t)n * sizeof(float), hipMemcpyHostToDevice, st);
     }
-    // the staging is reused by the next chunk: wait for these copies
-    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e == hipSuccess) e = hipEventRecord(stg.ev[set], st);
+    if (e != hipSuccess) return hip_fail(fn, "copy to device", e);
+  }
+  {
+    const hipError_t e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(fn, "copy to device", e);
   }
   for (int k = 0; k < 3; ++k)
