@@ -47,11 +47,13 @@ def _host(layout, bufs, S):
 
 
 @pytest.mark.parametrize("src_layout,dst_layout", [(SEP, SEP), (SEP, TILED), (TILED, SEP), (TILED, TILED)])
-@pytest.mark.parametrize("numels,world,rank", [([19_210], 4, 3), ([4_194_304 * 3 + 9_000], 3, 1)])
+@pytest.mark.parametrize("numels,world,rank", [([19_210], 4, 3), ([4_194_304 * 3 + 9_000], 3, 1),
+                                               ([(1 << 22) * 2], 2, 1), ([((1 << 21) + 1) * 3], 3, 2)])
 def test_save_read_load(src_layout, dst_layout, numels, world, rank, tmp_path):
-    """A shard of a few thousand elements, and one of about 4.2M (three 2M-element
+    """A shard of a few thousand elements; one of about 4.2M (three 2M-element
     staging chunks that alternate between the two staging sets, a ragged last
-    chunk and tile)."""
+    chunk and tile); exactly two full chunks; two chunks of which the last holds
+    one element."""
     plan = Z.Plan(numels, world)
     S = plan.shard_numel
     say(f"checkpoint S={S} {src_layout}->{dst_layout}")
