@@ -1,5 +1,6 @@
-"""The build's kernel-resource check: the compiler's resource-usage remarks are
-parsed per kernel, and a kernel that spills to scratch fails the build."""
+"""The build's kernel-resource check (the compiler's resource-usage remarks are
+parsed per kernel, and a kernel that spills to scratch fails the build), the
+benchmark's profile hash, and its refusal of more than one GPU."""
 from zero_sharded_mixed_plan_amd import build as B
 
 REMARKS = """\
@@ -37,3 +38,15 @@ def test_profile_hash_ignores_comments_only():
     assert base == 'int f(int x) {\n   return x + x;\n}\nconst char* s = "a // b";'
     assert bench._code_only(code.replace("twice", "double it")) == base
     assert bench._code_only(code.replace("x + x", "x * 2")) != base
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one rank on one GPU: --gpus above 1 exits with a
+    message before touching a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
