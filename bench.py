@@ -323,19 +323,22 @@ def run(name, steps, warmup, with_cpu, copy_gbps=None):
             raise RuntimeError("a replayed step overflowed on finite synthetic data")
         graph_ms = g0.elapsed_time(g1) / (reps * per)
         del graph
-    kernels = {}
+    kernels, per_launch = {}, {}
     if reduce_only:
         red = [evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)]
+        per_launch["reduce_kernel"] = red
         kernels["reduce_kernel"] = (sum(red) / steps, w.world * gb + 4)
         bpe_total = w.world * gb + 4
     elif clip:
         red = [evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)]
         upd = [evs[i][2].elapsed_time(evs[i][3]) for i in range(steps)]
+        per_launch["reduce_kernel"], per_launch["step_kernel_stash"] = red, upd
         kernels["reduce_kernel"] = (sum(red) / steps, w.world * gb + 4)
         kernels["step_kernel_stash"] = (sum(upd) / steps, 4 + 24 + pb)
         bpe_total = w.world * gb + 24 + pb + 8
     else:
         upd = [evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)]
+        per_launch["step_kernel"] = upd
         kernels["step_kernel"] = (sum(upd) / steps, n_read * gb + 24 + pb)
         bpe_total = n_read * gb + 24 + pb
     dom = max(kernels, key=lambda k: kernels[k][0])
@@ -368,6 +371,8 @@ def run(name, steps, warmup, with_cpu, copy_gbps=None):
             "algorithmic_bytes_per_element": bpe_total,
             "step_GBps": bpe_total * S / (ms_step * 1e-3) / 1e9,
             "kernel_ms": {k: round(v[0], 5) for k, v in kernels.items()},
+            "kernel_ms_median": {k: round(sorted(v)[len(v) // 2], 5) for k, v in per_launch.items()},
+            "kernel_ms_min": {k: round(min(v), 5) for k, v in per_launch.items()},
             "hip_graph_ms_per_step": graph_ms,
             "parallelism": "one rank of N (single GPU)",
             "stream_copy_GBps": copy_gbps,

@@ -31,6 +31,9 @@ def test_bench_line_toy():
     k_ms = c["kernel_ms"][r["kernel"]]   # reported to 1e-5 ms
     assert r["achieved"] == pytest.approx(r["bytes_per_element"] * 4803 / (k_ms * 1e-3) / 1e9,
                                           rel=1e-5 / k_ms)
+    for k in c["kernel_ms"]:   # per-launch HIP-event times: min <= median, min <= mean
+        assert 0 < c["kernel_ms_min"][k] <= c["kernel_ms_median"][k]
+        assert c["kernel_ms_min"][k] <= c["kernel_ms"][k] + 1e-5
     assert c["hip_graph_ms_per_step"] is not None and c["hip_graph_ms_per_step"] > 0
     cb = res["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["unit"] == "elements/s" and cb["cores"] >= 1 and cb["value"] > 0
