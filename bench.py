@@ -140,9 +140,19 @@ def cpu_baseline(w, slices, tiled_state, S, target_s=12.0, max_elems=1 << 26, ch
             if time.perf_counter() - t0 >= target_s or done >= 64 * n:
                 break
     dt = time.perf_counter() - t0
+    # the same oracle on one thread, over the first chunk, for about a tenth of the time
+    one, t1 = 0, time.perf_counter()
+    while True:
+        one += work(0)
+        if time.perf_counter() - t1 >= target_s / 10 or one >= 64 * min(n, chunk):
+            break
+    dt1 = time.perf_counter() - t1
     return {"value": done / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} elements of the rank's shard, stepped {done // n} time(s) "
-                      f"in {chunk}-element chunks on {threads} threads ({dt:.1f} s)"}
+                      f"in {chunk}-element chunks on {threads} threads ({dt:.1f} s)",
+            "value_1thread": one / dt1,
+            "sample_1thread": f"first {min(n, chunk)} elements, stepped {one // min(n, chunk)} time(s) "
+                              f"on one thread ({dt1:.1f} s)"}
 
 
 # ---------------------------------------------------------------------------

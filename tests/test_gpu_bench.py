@@ -37,3 +37,4 @@ def test_bench_line_toy():
     assert c["hip_graph_ms_per_step"] is not None and c["hip_graph_ms_per_step"] > 0
     cb = res["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["unit"] == "elements/s" and cb["cores"] >= 1 and cb["value"] > 0
+    assert cb["value_1thread"] > 0
