@@ -63,7 +63,8 @@ typedef enum { ZERO_F32 = 0, ZERO_BF16 = 1, ZERO_F16 = 2 } zero_dtype_t;
  *                       master[2048 t .. 2048 t + 2047], then m, then v of the
  *                       same elements (6144 floats).  The three state streams
  *                       become one read and one write stream, which the HBM
- *                       serves measurably faster than six.
+ *                       serves measurably faster than six.  Positions past S
+ *                       in the last tile are never read or written.
  */
 typedef enum { ZERO_STATE_SEPARATE = 0, ZERO_STATE_TILED = 1 } zero_state_layout_t;
 #define ZERO_STATE_TILE 2048

@@ -186,11 +186,12 @@ def test_world_and_alignment(world, rank, psi):
     run_workload(_flat(psi, world, rank, "bf16", "bf16"), layout=TILED)
 
 
-# Every compiled form of the slice reduction: 4 and 8 slices in narrow batches
-# (fp32: one or two batches of 4), 16 / 32 / 64 in wide batches (fp32: 8 per
-# batch), and 24, which no batch size divides (the runtime-N form), each in
-# the fused update and in the clipped path's reduction.
-@pytest.mark.parametrize("world", [4, 8, 16, 24, 32, 64])
+# Every compiled form of the slice reduction: 1, 2 and 4 slices in one batch of
+# exactly that many, 8 in one narrow batch (fp32: two batches of 4), 16 / 32 /
+# 64 in wide batches (fp32: 8 per batch), and 3 and 24, which no batch size
+# divides (the runtime-N form), each in the fused update and in the clipped
+# path's reduction.
+@pytest.mark.parametrize("world", [1, 2, 3, 4, 8, 16, 24, 32, 64])
 @pytest.mark.parametrize("g", ["f32", "bf16", "f16"])
 def test_batch_forms(world, g):
     psi = world * 4099

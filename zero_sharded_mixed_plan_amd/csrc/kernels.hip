@@ -965,7 +965,9 @@ __device__ __forceinline__ double wave_sum(double x) {
   return x;
 }
 
-template <class GT, bool WIDE, int NBATCH>
+// NB slices per load batch, NBATCH batches known at compile time (0: any N,
+// the runtime loop with batches of NB)
+template <class GT, int NB, int NBATCH>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) {
   // one 8-element vector per thread; workgroup b owns vectors [256 b, 256 b + 256),
   // so the partition (and every partial sum) depends only on S
@@ -982,7 +984,6 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) 
     const SegRange sr = a.grad_full ? wave_segs_v(a, v) : SegRange{0, -1};
     if (j0 + kVec <= a.S) {
       float acc[8], g[8];
-      constexpr int NB = Batch<GT, WIDE>::value;
       if constexpr (NBATCH > 0) {
         const char* ubase = static_cast<const char*>(a.grad) + blk * (kTile * GT::bytes);
         reduce8_fixed<GT, NB, NBATCH>(ubase, a.ld_bytes, threadIdx.x * (uint32_t)(kVec * GT::bytes), acc,
@@ -1403,33 +1404,61 @@ int launch_recast(const StepLaunch& a, zero_dtype_t pt, const u32* cond, void* s
   return check_launch("recast");
 }
 
-template <class GT, bool WIDE>
+// The reduction's batch forms: every whole number of batches of the usual
+// size (8 16-bit or 4 fp32 slices, twice that for larger N) in 1, 2 or 4
+// batches, and one batch of exactly N for N = 1, 2, 4 (the runtime loop, with
+// its per-slice guards, reduced 4 bf16 slices of the GPT-2 shard at 3.3 TB/s).
+// Only reachable forms are instantiated.
+template <class GT>
 static void go_reduce(const ReduceLaunch& a, dim3 grid, size_t lds, hipStream_t st) {
-  constexpr int NB = Batch<GT, WIDE>::value;
-  const int nbatch = (!a.grad_full && a.n % NB == 0) ? a.n / NB : 0;
   const dim3 blk(kThreads);
-  switch (nbatch) {
-    case 1: hipLaunchKernelGGL((reduce_kernel<GT, WIDE, 1>), grid, blk, lds, st, a); return;
-    case 2: hipLaunchKernelGGL((reduce_kernel<GT, WIDE, 2>), grid, blk, lds, st, a); return;
-    case 4: hipLaunchKernelGGL((reduce_kernel<GT, WIDE, 4>), grid, blk, lds, st, a); return;
-    default: hipLaunchKernelGGL((reduce_kernel<GT, WIDE, 0>), grid, blk, lds, st, a); return;
+  constexpr int NS = Batch<GT, false>::value, NW = Batch<GT, true>::value;
+  const int n = a.n;
+  if (!a.grad_full) {
+    if (n == 1) { hipLaunchKernelGGL((reduce_kernel<GT, 1, 1>), grid, blk, lds, st, a); return; }
+    if (n == 2) { hipLaunchKernelGGL((reduce_kernel<GT, 2, 1>), grid, blk, lds, st, a); return; }
+    if (n == NS) { hipLaunchKernelGGL((reduce_kernel<GT, NS, 1>), grid, blk, lds, st, a); return; }
+    if constexpr (NS == 8) {   // 16-bit: 4 alone is below the usual batch
+      if (n == 4) { hipLaunchKernelGGL((reduce_kernel<GT, 4, 1>), grid, blk, lds, st, a); return; }
+    } else {                   // fp32: 8 is two batches of 4
+      if (n == 2 * NS) { hipLaunchKernelGGL((reduce_kernel<GT, NS, 2>), grid, blk, lds, st, a); return; }
+    }
+    if (n > 8 && n % NW == 0) {
+      switch (n / NW) {
+        case 1:
+          if constexpr (NS == 8) {   // fp32 reaches 8 = NW as two batches of 4, above
+            hipLaunchKernelGGL((reduce_kernel<GT, NW, 1>), grid, blk, lds, st, a);
+            return;
+          }
+          break;
+        case 2: hipLaunchKernelGGL((reduce_kernel<GT, NW, 2>), grid, blk, lds, st, a); return;
+        case 4: hipLaunchKernelGGL((reduce_kernel<GT, NW, 4>), grid, blk, lds, st, a); return;
+        default: break;
+      }
+    }
   }
+  // the runtime loop: batches of the usual size, twice that above 8 buffers
+  if (n > 8) hipLaunchKernelGGL((reduce_kernel<GT, NW, 0>), grid, blk, lds, st, a);
+  else hipLaunchKernelGGL((reduce_kernel<GT, NS, 0>), grid, blk, lds, st, a);
 }
 
-template <class GT>
-static void go_reduce_wide(const ReduceLaunch& a, dim3 grid, size_t lds, hipStream_t st) {
-  if (a.n > 8) go_reduce<GT, true>(a, grid, lds, st);
-  else go_reduce<GT, false>(a, grid, lds, st);
+// Resident workgroups per CU of the reduction pass (eight elements per lane):
+// three while a lane's raw gradient bytes stay within 128 (16-bit N <= 8, fp32
+// N <= 4), else two.  Measured on the GPT-2 1.5B shard, 8 bf16 slices: 6.23
+// against 5.70 TB/s at two; 16 bf16 slices (Llama-3 shard) are best at two.
+static int reduce_blocks_per_cu(int n, int grad_bytes) {
+  return n * kVec * grad_bytes <= 128 ? kReduceFewBlocksPerCU : kStreamBlocksPerCU;
 }
 
 int launch_reduce(const ReduceLaunch& a, zero_dtype_t gt, int64_t nblocks, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  const size_t lds = occupancy_lds(stream_blocks_per_cu(a.n));
+  const int gb = gt == ZERO_F32 ? 4 : 2;
+  const size_t lds = occupancy_lds(reduce_blocks_per_cu(a.n, gb));
   const dim3 grid((unsigned)nblocks);
   switch (gt) {
-    case ZERO_F32: go_reduce_wide<TF32>(a, grid, lds, st); break;
-    case ZERO_BF16: go_reduce_wide<TBF16>(a, grid, lds, st); break;
-    case ZERO_F16: go_reduce_wide<TF16>(a, grid, lds, st); break;
+    case ZERO_F32: go_reduce<TF32>(a, grid, lds, st); break;
+    case ZERO_BF16: go_reduce<TBF16>(a, grid, lds, st); break;
+    case ZERO_F16: go_reduce<TF16>(a, grid, lds, st); break;
     default: return fail(ZERO_EINVAL, "unsupported gradient dtype");
   }
   return check_launch("reduce");

@@ -46,6 +46,7 @@ constexpr int kStashBlocksPerCU = 5;  // ... of the update kernel that reads the
 constexpr int kFewStreamBlocksPerCU = 3;  // ... of kernels that sum one or two gradient buffers
 constexpr int kNarrowBlocksPerCU = 3;     // ... of the four-element fused form
 constexpr int kNarrowWideBlocksPerCU = 2; // ... of that form with more than 64 raw gradient bytes per lane
+constexpr int kReduceFewBlocksPerCU = 3;  // ... of the reduction pass with at most 128 raw gradient bytes per lane
 constexpr size_t kStaticLdsRoom = 1024;  // LDS left for a streaming kernel's own __shared__ arrays
 constexpr int kSmallThreads = 1024;   // one-workgroup path for small shards ...
 constexpr int64_t kSmallShard = (int64_t)kSmallThreads * kVec;  // ... of at most this many elements
