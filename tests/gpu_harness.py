@@ -119,8 +119,38 @@ def compare_step(gpu_p, gpu_m, gpu_v, res: OS.StepResult, p_in, m_in, v_in, g_us
 
 
 # ---------------------------------------------------------------------------
+# the tiled state's last tile past S
+# ---------------------------------------------------------------------------
+
+# Tiled state buffers hold ceil(S / 2048) whole tiles; the positions past S in
+# the last tile's master, m and v belong to no element, and no kernel may read
+# them into an element or write them.  Tests plant this value there and check
+# that it is still there after every kind of step.
+TAIL_SENTINEL = -31.5
+
+
+def plant_tail(buf: torch.Tensor, S: int) -> None:
+    """Write TAIL_SENTINEL to a tiled state buffer's positions past S."""
+    T = Z.ZERO_STATE_TILE
+    if S % T:
+        buf.view(-1, 3, T)[-1, :, S % T:] = TAIL_SENTINEL
+
+
+def tail_intact(buf: torch.Tensor, S: int) -> bool:
+    """True if every position past S of a tiled buffer still holds the sentinel."""
+    T = Z.ZERO_STATE_TILE
+    if S % T == 0:
+        return True
+    return bool(torch.all(buf.view(-1, 3, T)[-1, :, S % T:] == TAIL_SENTINEL).item())
+
+
+# ---------------------------------------------------------------------------
 # one workload on the device
 # ---------------------------------------------------------------------------
+
+# every Rig made by the running test (the parity tests check their tiled
+# buffers' tails after each test)
+RIGS: list = []
 
 class Rig:
     """Device buffers of one rank for workload w (inputs drawn on the CPU)."""
@@ -148,9 +178,12 @@ class Rig:
             n = self.plan.state_numel(layout)
             self.A = [pack_state(master.to(dev), m.to(dev), v.to(dev), n)]
             self.B = [torch.zeros(n, dtype=torch.float32, device=dev)]
+            plant_tail(self.A[0], self.S)
+            plant_tail(self.B[0], self.S)
         else:
             self.A = [x.to(dev) for x in (master, m, v)]
             self.B = [torch.zeros(self.S, dtype=torch.float32, device=dev) for _ in range(3)]
+        RIGS.append(self)
         # gather buffer: a random bit pattern everywhere (to catch stray writes),
         # the rank's pieces hold the rounded initial master
         rng = np.random.default_rng(w.seed + 1)
@@ -213,6 +246,12 @@ class Rig:
                         skip_in=self.flag.data_ptr() if skip is True else skip,
                         **self.state_args(state, state), **self.common(t))
         Z.zero_adam_step(self.plan, a, torch.cuda.current_stream().cuda_stream)
+
+    def tails_intact(self) -> bool:
+        """Tiled layout: both state buffers still hold the sentinel past S."""
+        if self.layout != Z.ZERO_STATE_TILED:
+            return True
+        return tail_intact(self.A[0], self.S) and tail_intact(self.B[0], self.S)
 
     def gather_np(self):
         return storage(self.gather)

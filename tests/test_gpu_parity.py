@@ -8,8 +8,8 @@ import torch
 
 import workloads as W
 import zero_sharded_mixed_plan_amd as Z
-from gpu_harness import (CODE, Rig, check_params, compare_step, from_storage, guards, round_up,
-                         say, storage)
+from gpu_harness import (CODE, RIGS, Rig, check_params, compare_step, from_storage, guards, plant_tail,
+                         round_up, say, storage)
 from oracle import casts as OC
 from oracle import plan as OP
 from oracle import step as OS
@@ -22,6 +22,13 @@ F = np.float32
 def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
+    RIGS.clear()
+    yield
+    # no step of the test wrote a tiled state buffer past S (fused, clipped,
+    # skipped and restore steps all ran on these buffers)
+    bad = [r.w.name for r in RIGS if not r.tails_intact()]
+    RIGS.clear()
+    assert not bad, f"tiled state written past S: {bad}"
 
 
 def _oracle_slices(sl_cpu, S, world):
@@ -240,6 +247,8 @@ def test_overflow_skips_bitwise(bad, mode, layout, S):
     before = [x.clone() for x in rig.A]
     if mode == "fused":
         rig.B[0].fill_(7.0)
+        if layout == TILED:
+            plant_tail(rig.B[0], rig.S)
         rig.fused(sl_dev, rig.A, rig.B, 1)
     else:
         rig.reduce_norm(sl_dev)
@@ -262,10 +271,15 @@ def test_forced_skip(mode, layout, S):
     before = [x.clone() for x in rig.A]
     if mode == "fused":
         rig.B[-1].fill_(3.0)
+        if layout == TILED:
+            plant_tail(rig.B[0], rig.S)
         rig.fused(sl_dev, rig.A, rig.B, 1, skip=skip.data_ptr())
         torch.cuda.synchronize()
         assert rig.flag.item() == 1
-        assert torch.all(rig.B[-1] == 3.0)
+        if layout == TILED:
+            assert np.all(rig.unpack(rig.B)[2] == 3.0)
+        else:
+            assert torch.all(rig.B[-1] == 3.0)
     else:
         rig.reduce_norm(sl_dev)
         rig.stash_step(rig.A, 1, skip=skip.data_ptr())

@@ -13,7 +13,7 @@ import torch
 
 import workloads as W
 import zero_sharded_mixed_plan_amd as Z
-from gpu_harness import device_plan, oracle_layout, round_up, say
+from gpu_harness import device_plan, oracle_layout, plant_tail, round_up, say, tail_intact
 from zero_sharded_mixed_plan_amd.optim import dtype_code, pack_state, state_arg_dict, unpack_state
 
 pytestmark = pytest.mark.gpu
@@ -49,6 +49,8 @@ class Run:
 
     def reset(self):
         self.state = [self.init.clone(), torch.empty_like(self.init)]
+        for b in self.state:   # the positions past S are never written
+            plant_tail(b, self.S)
         self.cur = 0
         self.gather.zero_()
 
@@ -103,8 +105,9 @@ def test_concurrent_streams_match_serial():
     for r, ref in zip(runs, serial):
         got = r.result()
         assert int(got[2].item()) == 0 and int(ref[2].item()) == 0, r.w.name
-        # the S elements of master, m and v (the tiled buffer's last tile is
-        # never written past S: a fresh output buffer keeps whatever it held)
+        # the S elements of master, m and v; past S the last tile keeps the
+        # sentinel planted before the steps, in both buffers
+        assert all(tail_intact(b, r.S) for b in r.state), f"{r.w.name}: tiled state written past S"
         for name, a, b in zip(("master", "m", "v"), unpack_state(got[0], r.S), unpack_state(ref[0], r.S)):
             diff = (a.view(torch.int32) != b.view(torch.int32)).nonzero().flatten().cpu()
             assert diff.numel() == 0, (f"{r.w.name} {name}: {diff.numel()} of {r.S} differ, first at "
