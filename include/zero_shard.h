@@ -338,6 +338,9 @@ typedef struct zero_adam_args {
  *    swaps them only when *overflow_out == 0 after the step).  If the flag is
  *    set, the rank's gather slots are rewritten from master_in before the call's
  *    work completes, so they keep their pre-step values.
+ *    With overflow_out == NULL nothing is checked: the update is applied
+ *    whatever g holds (non-finite values included), and the state outputs may
+ *    then alias the inputs exactly (in place).
  *  - stash mode: the decision is known beforehand (skip_in = zero_shard_norm's
  *    overflow_out), so outputs may alias inputs (in place); overflow_out unused.
  *  - skip_in != NULL and *skip_in != 0 in either mode: the state outputs are

@@ -291,6 +291,69 @@ def test_forced_skip(mode, layout, S):
 
 @SIZES
 @LAYOUTS
+@pytest.mark.parametrize("why", ["inf", "skip_in"])
+def test_skip_rewrites_slots(why, layout, S):
+    """A fused step that is not applied leaves the rank's slots holding the
+    rounded input master, whatever they held before (the slots start as a
+    sentinel here, not as the rounded master the other tests start from), on
+    both sides of the one-workgroup path's limit; outside the slots nothing
+    changes."""
+    w = _flat(4 * S + 1, 4, 3, "bf16", "bf16")
+    rig = Rig(w, layout=layout)
+    sl_cpu, _ = rig.slices(1)
+    skip = None
+    if why == "inf":
+        sl_cpu[2, S // 2] = float("inf")
+    else:
+        skip = torch.ones(1, dtype=torch.int32, device="cuda")
+    mask = rig.slot_mask()
+    g0 = rig.gather0.copy()
+    g0[mask] = 0x3F80 if w.param_dtype != "f32" else 1.0   # bf16 1.0: not the rounded master
+    rig.gather.copy_(from_storage(g0, w.param_dtype).to("cuda"))
+    rig.fused(sl_cpu.to("cuda"), rig.A, rig.B, 1, skip=None if skip is None else skip.data_ptr())
+    torch.cuda.synchronize()
+    assert rig.flag.item() == 1
+    got = rig.gather_np()
+    assert np.array_equal(got[~mask], g0[~mask]), "write outside the rank's slots"
+    want = np.zeros_like(g0)
+    OS.write_gather(want, rig.lay.segments, OC.narrow(rig.p0, w.param_dtype))
+    assert np.array_equal(got[mask], want[mask]), "slots do not hold the rounded input master"
+
+
+@SIZES
+@LAYOUTS
+def test_no_flag_applies_update_with_inf(layout, S):
+    """Without an overflow flag nothing is checked: both paths apply the update
+    with the non-finite gradient, as the oracle's AdamW does without its skip."""
+    w = _flat(4 * S, 4, 1, "bf16", "bf16")
+    rig = Rig(w, layout=layout)
+    sl_cpu, _ = rig.slices(1)
+    sl_cpu[1, 77] = float("inf")
+    rig.fused(sl_cpu.to("cuda"), rig.A, rig.B, 1, overflow=False)
+    torch.cuda.synchronize()
+    sl = [storage(sl_cpu[k, :rig.S]) for k in range(4)]
+    g = OS.unscale(OS.average(OS.reduce_slices(sl, "bf16"), 4), 1.0)
+    with np.errstate(invalid="ignore", over="ignore"):
+        p2, m2, v2 = OS.adamw(rig.p0, rig.m0, rig.v0, g, OS.adam_consts(w.lr, w.beta1, w.beta2, w.eps,
+                                                                          w.weight_decay, 1))
+    gp, gm, gv = rig.unpack(rig.B)
+    # NaN bit patterns are not part of the contract (the CPU and the GPU make
+    # different default NaNs): NaN where the oracle has NaN, bits elsewhere
+    for a_, b_ in ((gp, p2), (gm, m2), (gv, v2)):
+        nan = np.isnan(b_)
+        assert np.array_equal(np.isnan(a_), nan)
+        assert np.array_equal(a_[~nan].view(np.uint32), b_[~nan].view(np.uint32))
+    assert np.isnan(gp[77]) and np.isinf(gm[77]) and np.isinf(gv[77])
+    got = rig.gather_np()
+    want = rig.gather0.copy()
+    OS.write_gather(want, rig.lay.segments, OC.narrow(p2, "bf16"))
+    is_nan16 = lambda x: ((x & 0x7F80) == 0x7F80) & ((x & 0x7F) != 0)
+    assert np.array_equal(is_nan16(got), is_nan16(want))
+    assert np.array_equal(got[~is_nan16(want)], want[~is_nan16(want)])
+
+
+@SIZES
+@LAYOUTS
 def test_no_flag_in_place_matches(layout, S):
     """Fused step without an overflow flag, updated in place."""
     w = _flat(4 * S + 3, 4, 3, "bf16", "bf16")

@@ -800,12 +800,30 @@ __device__ __forceinline__ void copy_state(const StepLaunch& a, int64_t j0, int 
   }
 }
 
+// The rank's gather slots of cnt local elements from j0 get the rounded p
+// (p[e] for e < cnt), with the widest stores a whole vector allows.
+template <class PT>
+__device__ __forceinline__ void store_slots(const StepLaunch& a, const SegRange& sr, int64_t j0, int cnt,
+                                            const float p[8]) {
+  if (cnt == kVec) {
+    const int64_t d0 = delta_of(a, sr, j0);
+    if (delta_of(a, sr, j0 + kVec - 1) == d0) {
+      store_params8<PT>(a.gather + (j0 + d0) * PT::bytes, p);
+      return;
+    }
+  }
+  for (int e = 0; e < cnt; ++e) store_param1<PT>(a.gather + (j0 + e + delta_of(a, sr, j0 + e)) * PT::bytes, p[e]);
+}
+
 // Small shards (S <= kSmallShard) in one launch: one workgroup, one 8-element
 // vector per thread.  Every thread reduces its slices first and keeps g in
 // registers; a workgroup-wide OR of the overflow decides the skip before any
-// output is written, so a skipped step writes nothing and needs no restore pass
-// or flag reset (the two extra launches of the multi-workgroup path, which
-// dominate a step this small).
+// output is written, so a skipped step needs no restore pass or flag reset
+// (the two extra launches of the multi-workgroup path, which dominate a step
+// this small).  A step that is not applied leaves what the multi-workgroup
+// path leaves: with an overflow flag, the rank's slots hold the rounded input
+// master (and with a.restore the output state holds the input state); without
+// one, nothing is checked and the update is applied whatever g holds.
 // (batches of 8 slices whatever N: 1024 threads leave 128 registers each)
 template <class GT, class PT>
 __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLaunch a) {
@@ -815,9 +833,14 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
   if (a.skip_in != nullptr && *a.skip_in != 0u) {
     if (a.overflow != nullptr && threadIdx.x == 0) *a.overflow = 1u;
     if (a.ctl != nullptr && threadIdx.x == 0) ctl_advance(a.ctl, true);
-    if (a.restore) {
-      const int64_t j = (int64_t)threadIdx.x * kVec, rest = a.S - j;
-      if (rest > 0) copy_state(a, j, rest >= kVec ? kVec : (int)rest);
+    const int64_t j = (int64_t)threadIdx.x * kVec, rest = a.S - j;
+    if (rest <= 0) return;
+    const int cnt = rest >= kVec ? kVec : (int)rest;
+    if (a.restore) copy_state(a, j, cnt);
+    if (a.overflow != nullptr) {   // the slots keep the pre-step parameters
+      float p[8];
+      for (int e = 0; e < cnt; ++e) p[e] = a.p_in[state_off(a, j + e)];
+      store_slots<PT>(a, wave_segs_v(a, threadIdx.x), j, cnt, p);
     }
     return;
   }
@@ -887,16 +910,18 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
     if (threadIdx.x == 0) ctl_advance(a.ctl, any_bad != 0);
   }
   if (cnt == 0) return;
-  if (any_bad) {
-    if (a.restore) {
-      if (cnt == kVec) {
+  if (any_bad && a.overflow != nullptr) {
+    if (cnt == kVec) {
+      if (a.restore) {
         st8(a.p_out + o0, p);
         st8(a.m_out + o0, m);
         st8(a.v_out + o0, v);
-      } else {
-        copy_state(a, j0, cnt);
       }
+    } else {
+      if (a.restore) copy_state(a, j0, cnt);
+      for (int e = 0; e < cnt; ++e) p[e] = a.p_in[state_off(a, j0 + e)];
     }
+    store_slots<PT>(a, sr, j0, cnt, p);   // the slots keep the pre-step parameters
     return;
   }
   if (cnt == kVec) {
@@ -905,12 +930,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
     st8(a.p_out + o0, p);
     st8(a.m_out + o0, m);
     st8(a.v_out + o0, v);
-    const int64_t d0 = delta_of(a, sr, j0);
-    if (delta_of(a, sr, j0 + kVec - 1) == d0) {
-      store_params8<PT>(a.gather + (j0 + d0) * PT::bytes, p);
-    } else {
-      for (int e = 0; e < 8; ++e) store_param1<PT>(a.gather + (j0 + e + delta_of(a, sr, j0 + e)) * PT::bytes, p[e]);
-    }
+    store_slots<PT>(a, sr, j0, kVec, p);
   } else {
     for (int e = 0; e < cnt; ++e) {
       const int64_t j = j0 + e;
