@@ -466,9 +466,12 @@ typedef struct zero_ckpt_meta {
  * step and loss-scale fields for consistency (step >= 0, scale finite and >=
  * 0, growth_factor > 1, backoff_factor in (0, 1), 0 <= growth_tracker <
  * growth_interval), then
+ * verifies the three checksums in a read-only pass over the file; only then
  * copies the shard into the device state on `stream` and waits for it.  A
- * checksum mismatch is found only after the data has been copied: then the
- * device state is undefined and ZERO_EIO is returned.
+ * corrupt file is refused with ZERO_EIO before anything is copied, leaving the
+ * device state as it was (if the file changes between the two passes, the
+ * second pass's checksums catch it: ZERO_EIO, device state undefined).  With
+ * the tiled layout, positions past S in the last tile are not written.
  * Errors: ZERO_EINVAL (arguments, or a file for another plan or rank),
  * ZERO_EALIGN, ZERO_EIO, ZERO_ENOMEM, ZERO_EHIP.
  */

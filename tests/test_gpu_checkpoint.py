@@ -12,7 +12,7 @@ import torch
 import workloads as W
 import zero_sharded_mixed_plan_amd as Z
 from ckpt_format import fnv1a, read
-from gpu_harness import oracle_layout, say
+from gpu_harness import oracle_layout, plant_tail, say, tail_intact
 from zero_sharded_mixed_plan_amd.optim import ZeroAdam, pack_state, unpack_state
 
 pytestmark = pytest.mark.gpu
@@ -76,15 +76,15 @@ def test_save_read_load(src_layout, dst_layout, numels, world, rank, tmp_path):
         if S < 100_000:
             assert f["sums"][k] == fnv1a(f[name].tobytes())
     dst = _device(dst_layout, plan, [torch.full((S,), 7.0) for _ in range(3)])
+    if dst_layout == TILED:
+        plant_tail(dst[0], S)
     meta = Z.zero_checkpoint_load(plan, rank, path, dst_layout, *_ptrs(dst_layout, dst),
                                   torch.cuda.current_stream().cuda_stream)
     assert meta.step == 42 and meta.scaler.scale == 1024.0 and meta.scaler.growth_tracker == 1
     for k, a in enumerate(_host(dst_layout, dst, S)):
         assert np.array_equal(a.view(np.uint32), arrays[k].numpy().view(np.uint32))
-    if dst_layout == TILED:   # the last tile's tail past S is zero
-        T = Z.ZERO_STATE_TILE
-        tail = dst[0].view(-1, 3, T)[-1].cpu().numpy()[:, S % T:] if S % T else np.zeros(1)
-        assert np.all(tail == 0)
+    if dst_layout == TILED:   # the last tile's positions past S are not written
+        assert tail_intact(dst[0], S)
 
 
 def test_corrupt_and_foreign_files(tmp_path):
@@ -103,9 +103,13 @@ def test_corrupt_and_foreign_files(tmp_path):
     raw = bytearray(open(path, "rb").read())
     raw[128 + 4 * S + 17] ^= 0x40                            # one bit of m
     open(path, "wb").write(bytes(raw))
+    for b in bufs:            # the live state a failed load must leave alone
+        b.fill_(7.0)
     with pytest.raises(Z.ZeroError) as e:
         Z.zero_checkpoint_load(plan, 2, path, SEP, *_ptrs(SEP, bufs), st)
     assert e.value.code == Z.ZERO_EIO and "checksum" in Z.zero_last_error()
+    torch.cuda.synchronize()
+    assert all(bool(torch.all(b == 7.0)) for b in bufs), "a corrupt file was copied into the state"
 
 
 @pytest.mark.parametrize("layout", [SEP, TILED])

@@ -144,3 +144,29 @@ def test_checkpoint_load_rejects_foreign_files(case, code, tmp_path):
     with pytest.raises(Z.ZeroError) as e:
         _load(plan, str(path))
     assert e.value.code == code, Z.zero_last_error()
+
+
+def test_checkpoint_load_checks_sums_before_copying(tmp_path):
+    """A file with a valid header and size whose data do not match its
+    checksums is refused by the read-only pass, before any copy to the device:
+    the destination pointers here are never dereferenced (there is no GPU), so
+    reaching the copy would fail differently.  The same file with the right
+    sums gets past that pass (and only then needs the device)."""
+    from ckpt_format import fnv1a
+    plan = Z.Plan([100], 4)                          # S = 25
+    S = 25
+    arrays = [np.arange(S, dtype=np.float32) * (k + 1) for k in range(3)]
+    body = b"".join(a.tobytes() for a in arrays)
+    sums = [fnv1a(a.tobytes()) for a in arrays]
+    path = tmp_path / "shard"
+    bad = list(sums)
+    bad[1] ^= 1
+    path.write_bytes(header(Z.zero_plan_hash(plan), 4, 1, S, sums=tuple(bad)) + body)
+    with pytest.raises(Z.ZeroError) as e:
+        _load(plan, str(path))
+    assert e.value.code == Z.ZERO_EIO
+    assert "checksum mismatch (nothing was copied" in Z.zero_last_error()
+    path.write_bytes(header(Z.zero_plan_hash(plan), 4, 1, S, sums=tuple(sums)) + body)
+    with pytest.raises(Z.ZeroError) as e:
+        _load(plan, str(path))
+    assert "checksum" not in Z.zero_last_error()

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -348,11 +349,39 @@ extern "C" int zero_checkpoint_load(const zero_plan_t* plan, int32_t rank, const
       (long long)ftello(in.f) != (long long)kHeader + 3LL * S * (long long)sizeof(float))
     return fail(ZERO_EIO, std::string(fn) + ": file size does not match the shard");
 
+  const int64_t nchunks = (S + kChunk - 1) / kChunk;
+  // Pass 1, host only and read only: the checksums are verified before
+  // anything reaches the device, so a corrupt file leaves the caller's state
+  // as it was.
+  {
+    const size_t len = (size_t)(S < kChunk ? S : kChunk);
+    std::vector<float> buf;
+    try {
+      buf.resize(3 * len);
+    } catch (const std::bad_alloc&) {
+      return fail(ZERO_ENOMEM, std::string(fn) + ": host buffer");
+    }
+    uint64_t sum[3] = {kFnvOffset, kFnvOffset, kFnvOffset};
+    for (int64_t c = 0; c < nchunks; ++c) {
+      const int64_t j0 = c * kChunk, n = (S - j0 < kChunk) ? S - j0 : kChunk;
+      for (int k = 0; k < 3; ++k) {
+        const long long off = (long long)kHeader + ((long long)k * S + j0) * (long long)sizeof(float);
+        if (fseeko(in.f, (off_t)off, SEEK_SET) != 0 ||
+            std::fread(buf.data() + k * len, sizeof(float), (size_t)n, in.f) != (size_t)n)
+          return fail(ZERO_EIO, std::string(fn) + ": read failed");
+      }
+      fnv3(sum, buf.data(), buf.data() + len, buf.data() + 2 * len, (size_t)n * sizeof(float));
+    }
+    for (int k = 0; k < 3; ++k)
+      if (sum[k] != get_u64(h, 72 + 8 * k))
+        return fail(ZERO_EIO, std::string(fn) + ": checksum mismatch (nothing was copied to the device)");
+  }
   Staging stg;
   if (stg.alloc(st) != hipSuccess || !stg.buf) return fail(ZERO_ENOMEM, std::string(fn) + ": pinned staging");
+  // Pass 2: the copy to the device (hashed again, in case the file changed
+  // between the passes).
   uint64_t sum[3] = {kFnvOffset, kFnvOffset, kFnvOffset};
   float* dst[3] = {master, m, v};
-  const int64_t nchunks = (S + kChunk - 1) / kChunk;
   for (int64_t c = 0; c < nchunks; ++c) {
     const int set = (int)(c & 1);
     const int64_t j0 = c * kChunk, n = (S - j0 < kChunk) ? S - j0 : kChunk;
@@ -370,16 +399,23 @@ extern "C" int zero_checkpoint_load(const zero_plan_t* plan, int32_t rank, const
     fnv3(sum, stg.arr(set, 0), stg.arr(set, 1), stg.arr(set, 2), (size_t)n * sizeof(float));
     hipError_t e = hipSuccess;
     if (tiled) {
-      const int64_t t0 = j0 / zk::kStateTile, nt = (n + zk::kStateTile - 1) / zk::kStateTile;
+      // whole tiles in one copy; a partial last tile (the shard's end) as its
+      // three valid runs, so nothing past S is written
+      const int64_t T = zk::kStateTile;
+      const int64_t t0 = j0 / T, nfull = n / T, rest = n % T;
       float* tb = stg.tiles(set);
-      for (int64_t t = 0; t < nt; ++t)
+      for (int64_t t = 0; t < nfull + (rest ? 1 : 0); ++t)
         for (int k = 0; k < 3; ++k)
-          for (int64_t r = 0; r < zk::kStateTile; ++r) {
-            const int64_t i = t * zk::kStateTile + r;
-            tb[(t * 3 + k) * zk::kStateTile + r] = i < n ? stg.arr(set, k)[i] : 0.0f;  // past S: zeros
+          for (int64_t r = 0; r < T; ++r) {
+            const int64_t i = t * T + r;
+            tb[(t * 3 + k) * T + r] = i < n ? stg.arr(set, k)[i] : 0.0f;
           }
-      e = hipMemcpyAsync(master + t0 * 3 * zk::kStateTile, tb, (size_t)nt * 3 * zk::kStateTile * sizeof(float),
-                         hipMemcpyHostToDevice, st);
+      if (nfull > 0)
+        e = hipMemcpyAsync(master + t0 * 3 * T, tb, (size_t)nfull * 3 * T * sizeof(float), hipMemcpyHostToDevice,
+                           st);
+      for (int k = 0; k < 3 && rest && e == hipSuccess; ++k)
+        e = hipMemcpyAsync(master + ((t0 + nfull) * 3 + k) * T, tb + (nfull * 3 + k) * T,
+                           (size_t)rest * sizeof(float), hipMemcpyHostToDevice, st);
     } else {
       for (int k = 0; k < 3 && e == hipSuccess; ++k)
         e = hipMemcpyAsync(dst[k] + j0, stg.arr(set, k), (size_t)n * sizeof(float), hipMemcpyHostToDevice, st);
@@ -393,7 +429,8 @@ extern "C" int zero_checkpoint_load(const zero_plan_t* plan, int32_t rank, const
   }
   for (int k = 0; k < 3; ++k)
     if (sum[k] != get_u64(h, 72 + 8 * k))
-      return fail(ZERO_EIO, std::string(fn) + ": checksum mismatch (the device state is now undefined)");
+      return fail(ZERO_EIO, std::string(fn) + ": the file changed while it was loaded (the device state is "
+                                              "now undefined)");
   meta->step = (int64_t)get_u64(h, 40);
   meta->scaler.scale = get_f32(h, 48);
   meta->scaler.growth_tracker = (int32_t)get_u32(h, 52);
