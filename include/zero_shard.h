@@ -148,6 +148,10 @@ int zero_plan_rank_segment(const zero_plan_t* plan, int32_t rank, int32_t b, int
  *   3: 16 Psi / N.
  * formula_bytes gets the formula with the unpadded Psi; padded_bytes the same
  * with N*S for Psi and S for Psi/N (the bytes this layout really holds).
+ * The pages' formulas fix 2-byte (fp16) parameters and gradients next to
+ * 12 bytes of fp32 optimizer state per parameter, so the call takes no
+ * parameter-byte argument: the accounting of other storage types is not on
+ * the pages.
  */
 int zero_plan_bytes(const zero_plan_t* plan, int32_t stage, double* formula_bytes,
                     int64_t* padded_bytes);
@@ -226,6 +230,13 @@ typedef struct zero_step_ctl zero_step_ctl_t;
 /*
  * Gradient preparation, first pass of the clipped step (global-norm clipping
  * needs the norm of the whole gradient before any element is updated).
+ * The reduction, average and unscale are those of the fused step: the SUM of
+ * the reduce-scatter and g /= world of zero_adam.py (handbook chapter "ZeRO 与
+ * FSDP：切分优化器状态、梯度与参数", section "从零实现 ZeRO 的 Adam") and
+ * GradScaler's unscale ("PaddlePaddle ZeRO优化…", section "混合精度才是最佳
+ * 拍档").  Global-norm clipping itself is not described on any of the pages:
+ * the sum of squares written here and its use in zero_shard_norm are this
+ * library's reading (textbook clipping by the global L2 norm).
  *
  * For every local element j < S, with C = grad_count (0 means N):
  *   acc = buf_0[j] + buf_1[j] + ... + buf_{C-1}[j]           (fp32, ascending k)
@@ -259,7 +270,13 @@ int zero_reduce_shard(const zero_plan_t* plan, int32_t rank, const void* grad, i
 /*
  * Second pass: finalize what zero_reduce_shard left in `ws` (two small launches:
  * 256 workgroups sum fixed ranges of the per-workgroup partials into `ws`, one
- * workgroup sums those in index order).
+ * workgroup sums those in index order).  The overflow word is GradScaler's
+ * inf/NaN check, on which the step is skipped ("PaddlePaddle ZeRO优化…",
+ * section "混合精度才是最佳拍档").  The norm and the clip coefficient are not
+ * on the pages (they never mention clipping): this is the textbook global-norm
+ * clip, c = max_norm / ||g|| when ||g|| exceeds max_norm, with ||g|| taken over
+ * the unclipped, unscaled gradient of every rank and the coefficient rounded
+ * once to fp32 -- a reading, not a passage of the pages.
  *   overflow_out (device u32): 1 if any g was non-finite, else 0.
  *   q = sum of the partial sums in a fixed order; Q = q + other_ranks_sumsq (the
  *   other ranks' share of the global sum, 0 on one rank); norm = sqrt(Q) (fp64).
