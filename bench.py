@@ -9,11 +9,13 @@ workload, the two-pass global-norm clip), AdamW on the fp32 master/m/v, and the
 rounded parameters written into the rank's slots of the all-gather buffer.
 Inputs are seeded synthetic data resident in HBM before the timed region.
 
-Prints ONE JSON line (the default workload: GPT-2 1.5B shapes, N = 8, rank 7,
-bf16 slices and parameters).  `--workload all` also writes one line per
-workload to stderr (and to --report if given), and prints the default
-workload's line last on stdout; there the oracle is timed on the host beside
-each of the five workloads (`cpu_baseline`, a bounded sample of each).
+Prints ONE JSON line (the default workload, the largest one: the Llama-7B-like
+tensor list, N = 8, rank 7, a shard of 842,301,952 elements, bf16 slices and
+parameters, fp32 master/m/v; the oracle is timed on one full step over it).
+`--workload all` also writes one line per workload to stderr (and to --report
+if given), and prints the default workload's line last on stdout; there the
+oracle is timed on the host beside each of the five workloads (`cpu_baseline`:
+a bounded sample of each, one whole step for the default workload).
 """
 from __future__ import annotations
 
@@ -27,7 +29,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-DEFAULT = "gpt2_1p5b_n8"
+DEFAULT = "llama_7b_n8"
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published peak
 METRIC = "shard elements/sec of fused ZeRO AdamW step; achieved HBM GB/s vs peak"
 
@@ -99,7 +101,13 @@ def load_traffic(kernel: str, workload: str):
 # the CPU oracle, timed on a bounded sample (cpu_baseline)
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(w, slices, tiled_state, S, target_s=12.0, max_elems=1 << 26, chunk=1 << 20):
+def cpu_baseline(w, slices, tiled_state, S, full_step=False, target_s=5.0, max_elems=1 << 26,
+                 chunk=1 << 20):
+    """The oracle as written, timed on the host's cores.  full_step: one whole
+    step over all S elements of the rank's shard (inputs copied to the host
+    first, the oracle's arithmetic alone is timed); otherwise a bounded sample,
+    the first max_elems elements stepped repeatedly for about target_s.  Both
+    also time one thread on the first chunk."""
     import concurrent.futures as cf
 
     import numpy as np
@@ -107,12 +115,16 @@ def cpu_baseline(w, slices, tiled_state, S, target_s=12.0, max_elems=1 << 26, ch
 
     import zero_sharded_mixed_plan_amd as Z
     from oracle import step as OS
-    from zero_sharded_mixed_plan_amd.optim import unpack_state
 
     threads = max(1, min(os.cpu_count() or 1, 16))
-    n = min(S, max_elems)
-    n -= n % chunk if n > chunk else 0
-    n = max(n, min(S, chunk))
+    if full_step:
+        n = S
+    else:
+        n = min(S, max_elems)
+        n -= n % chunk if n > chunk else 0
+        n = max(n, min(S, chunk))
+    T = Z.ZERO_STATE_TILE
+    chunk = max(T, chunk // T * T)
 
     def host(t):
         t = t.detach().cpu().contiguous()
@@ -120,9 +132,12 @@ def cpu_baseline(w, slices, tiled_state, S, target_s=12.0, max_elems=1 << 26, ch
             return t.view(torch.int16).numpy().view(np.uint16)
         return t.numpy()
 
+    t_copy = time.perf_counter()
     sl = [host(slices[k, :n]) for k in range(w.world)]
-    T = Z.ZERO_STATE_TILE
-    p, m, v = (host(x) for x in unpack_state(tiled_state[:(n + T - 1) // T * 3 * T], n))
+    st = host(tiled_state[:(n + T - 1) // T * 3 * T]).reshape(-1, 3, T)
+    p, m, v = (np.ascontiguousarray(st[:, i, :].reshape(-1)[:n]) for i in range(3))
+    del st
+    t_copy = time.perf_counter() - t_copy
     kw = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
               t=w.t0 + 1, inv_scale=1.0 / w.loss_scale, max_norm=w.max_norm)
 
@@ -137,19 +152,22 @@ def cpu_baseline(w, slices, tiled_state, S, target_s=12.0, max_elems=1 << 26, ch
     with cf.ThreadPoolExecutor(threads) as ex:
         while True:
             done += sum(ex.map(work, range(0, n, chunk)))
-            if time.perf_counter() - t0 >= target_s or done >= 64 * n:
+            if full_step or time.perf_counter() - t0 >= target_s or done >= 64 * n:
                 break
     dt = time.perf_counter() - t0
-    # the same oracle on one thread, over the first chunk, for about a tenth of the time
+    # the same oracle on one thread, over the first chunk
     one, t1 = 0, time.perf_counter()
     while True:
         one += work(0)
-        if time.perf_counter() - t1 >= target_s / 10 or one >= 64 * min(n, chunk):
+        if time.perf_counter() - t1 >= max(0.5, dt / 10) or one >= 64 * min(n, chunk):
             break
     dt1 = time.perf_counter() - t1
+    what = (f"one full step over all {n} elements of the rank's shard" if full_step else
+            f"first {n} of the shard's {S} elements, stepped {done // n} time(s)")
     return {"value": done / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} elements of the rank's shard, stepped {done // n} time(s) "
-                      f"in {chunk}-element chunks on {threads} threads ({dt:.1f} s)",
+            "sample": f"{what} in {chunk}-element chunks on {threads} threads ({dt:.2f} s of "
+                      f"wall time; inputs copied to the host beforehand in {t_copy:.1f} s, not timed)",
+            "seconds": dt, "elements": done,
             "value_1thread": one / dt1,
             "sample_1thread": f"first {min(n, chunk)} elements, stepped {one // min(n, chunk)} time(s) "
                               f"on one thread ({dt1:.1f} s)"}
@@ -172,7 +190,7 @@ VARIANTS = {
 }
 
 
-def run(name, steps, warmup, with_cpu, copy_gbps=None):
+def run(name, steps, warmup, with_cpu, copy_gbps=None, ld_pad=0):
     import dataclasses
 
     import torch
@@ -197,7 +215,7 @@ def run(name, steps, warmup, with_cpu, copy_gbps=None):
         plan.attach_piece_table(w.rank, table.data_ptr(), table.numel())
     S = plan.shard_numel
     lay = W.Layout(S=S, segments=plan.segments(w.rank), tensor_flat_off=plan.tensor_offsets())
-    ld = round_up(S, 64)
+    ld = round_up(S, 64) + ld_pad
     log(f"[bench] {name}: S={S} N={w.world} rank={w.rank} buckets={plan.num_buckets} "
         f"grads={w.grad_dtype} params={w.param_dtype} clip={w.max_norm}")
 
@@ -366,6 +384,8 @@ def run(name, steps, warmup, with_cpu, copy_gbps=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        # the type the step computes in (every workload reduces, updates and
+        # keeps its state in fp32); the storage types are in config below
         "dtype": "f32",
         "data": "synthetic",
         "config": {
@@ -376,7 +396,8 @@ def run(name, steps, warmup, with_cpu, copy_gbps=None):
             "plan_layout": {"flat": "flat buckets", "dim0": "per-parameter dim-0 (FSDP2)"}[plan_layout],
             "piece_table": table is not None,
             "shard_elements": S, "world": w.world, "rank": w.rank,
-            "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype, "buckets": plan.num_buckets,
+            "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype, "state_dtype": "f32",
+            "buckets": plan.num_buckets,
             "clip": clip and not reduce_only, "state_layout": "tiled",
             "algorithmic_bytes_per_element": bpe_total,
             "step_GBps": bpe_total * S / (ms_step * 1e-3) / 1e9,
@@ -394,8 +415,9 @@ def run(name, steps, warmup, with_cpu, copy_gbps=None):
                      "traffic": traffic},
     }
     if with_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, slices, state["cur"][0], S,
-                                           target_s=12.0 if name == DEFAULT else 5.0)
+        # the headline workload: one whole oracle step over the shard; the
+        # others: a bounded sample of theirs
+        out["cpu_baseline"] = cpu_baseline(w, slices, state["cur"][0], S, full_step=(name == DEFAULT))
     del slices, A, B, gather
     torch.cuda.empty_cache()
     return out
@@ -452,7 +474,7 @@ def copy_probe(steps, warmup, gib=4.0):
     print(json.dumps(out), flush=True)
 
 
-def checkpoint_probe(name=DEFAULT, reps=2):
+def checkpoint_probe(name="gpt2_1p5b_n8", reps=2):
     """Sharded checkpoint of one rank's optimizer state (master, m, v in the
     tiled device layout; 12 B per shard element on disk plus a 128-byte header):
     save and load through the library, timed on the host clock, bytes of the
