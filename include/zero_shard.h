@@ -289,6 +289,34 @@ int zero_shard_norm(const zero_plan_t* plan, void* ws, double other_ranks_sumsq,
                     double max_norm, uint32_t* overflow_out, double* sumsq_out,
                     float* clip_coef_out, void* stream);
 
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the two
+ * calls above in one, with their workspace in a fixed array inside the
+ * library instead of a caller buffer.  Equivalent to
+ *   zero_reduce_shard(plan, rank, grad, grad_ld, grad_count, grad_layout,
+ *                     grad_dtype, inv_scale, g_out, ws, 1, ctl, stream);
+ *   zero_shard_norm(plan, ws, other_ranks_sumsq, max_norm, overflow_out,
+ *                   sumsq_out, clip_coef_out, stream);
+ * with every argument as documented there, and the same results bit for bit.
+ * The array holds ZERO_NOALLOC_SCRATCH_BYTES (4 MiB) on every GPU the library
+ * runs on, until the process ends: shards of at most
+ * zero_noalloc_max_shard() elements (715,302,912); a larger plan is refused
+ * with ZERO_EINVAL before anything is enqueued.  The call allocates no device
+ * memory (its first call on a device looks up that device's array).  Every
+ * call on one GPU uses that GPU's one array, so calls that overlap in time on
+ * one GPU (on different streams, or from several threads) race and give
+ * undefined results; calls ordered on one stream are safe.  Nothing in the
+ * array needs to start at zero: every call writes each word it reads.
+ * Errors: as the two calls, and ZERO_EINVAL for a shard beyond the limit.
+ */
+#define ZERO_NOALLOC_SCRATCH_BYTES (4 * 1024 * 1024)
+int64_t zero_noalloc_max_shard(void);
+int zero_reduce_norm_noalloc(const zero_plan_t* plan, int32_t rank, const void* grad, int64_t grad_ld,
+                             int32_t grad_count, int32_t grad_layout, zero_dtype_t grad_dtype, float inv_scale,
+                             float* g_out, double other_ranks_sumsq, double max_norm, uint32_t* overflow_out,
+                             double* sumsq_out, float* clip_coef_out, zero_step_ctl_t* ctl, void* stream);
+
 /* Arguments of zero_adam_step (host struct; pointers are device addresses). */
 typedef struct zero_adam_args {
   int32_t rank;              /* 0 <= rank < N                                      */

@@ -12,7 +12,8 @@ from ._abi import (DTYPE_BYTES, DTYPE_CODES, EXPORTS, ZERO_BF16, ZERO_EALIGN, ZE
                    Plan, Scaler, ZeroError, adam_args, lib, zero_adam_args_t, zero_adam_step,
                    zero_checkpoint_load, zero_checkpoint_save, zero_ckpt_meta_t, zero_last_error,
                    zero_plan_hash, zero_reduce_shard, zero_scaler_t, zero_shard_norm, zero_step_ctl_t,
-                   zero_stream_copy, zero_version)
+                   zero_stream_copy, zero_version, ZERO_NOALLOC_SCRATCH_BYTES, zero_noalloc_max_shard,
+                   zero_reduce_norm_noalloc)
 
 __all__ = [
     "DTYPE_BYTES", "DTYPE_CODES", "EXPORTS", "ZERO_BF16", "ZERO_EALIGN", "ZERO_EHIP", "ZERO_EINVAL",
@@ -21,5 +22,5 @@ __all__ = [
     "adam_args", "lib", "zero_adam_args_t", "zero_adam_step", "zero_checkpoint_load",
     "zero_checkpoint_save", "zero_ckpt_meta_t", "zero_last_error", "zero_plan_hash",
     "zero_reduce_shard", "zero_scaler_t", "zero_shard_norm", "zero_step_ctl_t", "zero_stream_copy",
-    "zero_version",
+    "zero_version", "ZERO_NOALLOC_SCRATCH_BYTES", "zero_noalloc_max_shard", "zero_reduce_norm_noalloc",
 ]

@@ -28,8 +28,8 @@ EXPORTS = [
     "zero_plan_padded_numel", "zero_plan_world", "zero_plan_num_buckets", "zero_plan_num_tensors",
     "zero_plan_bucket", "zero_plan_tensor", "zero_plan_rank_segment", "zero_plan_bytes",
     "zero_state_numel", "zero_workspace_bytes", "zero_plan_piece_table_bytes", "zero_plan_attach_piece_table",
-    "zero_reduce_shard", "zero_shard_norm", "zero_adam_step",
-    "zero_scaler_init", "zero_scaler_update", "zero_scaler_inv_scale", "zero_plan_hash",
+    "zero_reduce_shard", "zero_shard_norm", "zero_noalloc_max_shard", "zero_reduce_norm_noalloc",
+    "zero_adam_step", "zero_scaler_init", "zero_scaler_update", "zero_scaler_inv_scale", "zero_plan_hash",
     "zero_checkpoint_save", "zero_checkpoint_load", "zero_stream_copy", "zero_last_error", "zero_version",
 ]
 
@@ -143,6 +143,9 @@ def load(path: str, required: bool = True) -> ctypes.CDLL:
         "zero_plan_attach_piece_table": (ctypes.c_int, [vp, i32, vp, i64]),
         "zero_reduce_shard": (ctypes.c_int, [vp, i32, vp, i64, i32, i32, ctypes.c_int, f32, vp, vp, i32, vp, vp]),
         "zero_shard_norm": (ctypes.c_int, [vp, vp, f64, f64, vp, vp, vp, vp]),
+        "zero_noalloc_max_shard": (i64, []),
+        "zero_reduce_norm_noalloc": (ctypes.c_int, [vp, i32, vp, i64, i32, i32, ctypes.c_int, f32, vp, f64, f64,
+                                                    vp, vp, vp, vp, vp]),
         "zero_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(zero_adam_args_t), vp]),
         "zero_scaler_init": (ctypes.c_int, [ctypes.POINTER(zero_scaler_t), f32, f32, f32, i32]),
         "zero_scaler_update": (ctypes.c_int, [ctypes.POINTER(zero_scaler_t), i32]),
@@ -323,6 +326,25 @@ def zero_shard_norm(plan: Plan, ws: int, other_ranks_sumsq: float, max_norm: flo
                     overflow_out: int, sumsq_out: int, clip_coef_out: int, stream: int = 0) -> None:
     _check(lib().zero_shard_norm(plan.handle, ws, other_ranks_sumsq, max_norm, overflow_out or None,
                                  sumsq_out or None, clip_coef_out or None, stream or None))
+
+
+ZERO_NOALLOC_SCRATCH_BYTES = 4 * 1024 * 1024
+
+
+def zero_noalloc_max_shard() -> int:
+    return int(lib().zero_noalloc_max_shard())
+
+
+def zero_reduce_norm_noalloc(plan: Plan, grad: int, grad_ld: int, grad_dtype: int, inv_scale: float,
+                             g_out: int, other_ranks_sumsq: float, max_norm: float, overflow_out: int,
+                             sumsq_out: int, clip_coef_out: int, stream: int = 0, grad_count: int = 0,
+                             grad_layout: int = ZERO_GRAD_SHARD, rank: int = 0, ctl: int = 0) -> None:
+    """zero_reduce_shard + zero_shard_norm with the library's fixed workspace
+    (for callers that cannot allocate device memory)."""
+    _check(lib().zero_reduce_norm_noalloc(plan.handle, int(rank), grad, grad_ld, grad_count, grad_layout,
+                                          grad_dtype, inv_scale, g_out or None, other_ranks_sumsq, max_norm,
+                                          overflow_out or None, sumsq_out or None, clip_coef_out or None,
+                                          ctl or None, stream or None))
 
 
 def zero_adam_step(plan: Plan, args: zero_adam_args_t, stream: int = 0) -> None:

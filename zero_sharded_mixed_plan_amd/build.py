@@ -20,7 +20,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libzero_shard.so")
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("kernels.hip", "abi.cpp", "plan.cpp", "runtime.cpp")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("kernels.hip", "abi.cpp", "plan.cpp", "runtime.cpp", "noalloc.hip")]
 ARCH = "gfx950"
 
 FLAGS = [
