@@ -711,13 +711,13 @@ template <> __device__ __forceinline__ void widen4<TF32>(const Raw4<TF32>& r, fl
 // stored output -4%, N = 2 -3%, N = 4 -12%, N = 32 -8%; 7.5B N = 64 -2%;
 // Llama-7B N = 16 -6%; fp32 gradients -8 to -11%).  Lane t takes elements
 // [4 q, 4 q + 4), q = 2 v_lo + t.
-template <class GT, class PT, int C>
-__global__ __launch_bounds__(kThreads) void narrow_step_kernel(const StepLaunch a) {
+template <class GT, class PT, int C, int TPB = kThreads>
+__global__ __launch_bounds__(TPB) void narrow_step_kernel(const StepLaunch a) {
   if (a.skip_in != nullptr && *a.skip_in != 0u) {
     if (a.overflow != nullptr && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.overflow, 1u);
     return;
   }
-  const int64_t q = 2 * a.v_lo + (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t q = 2 * a.v_lo + (int64_t)blockIdx.x * TPB + threadIdx.x;
   const int64_t j0 = q * 4;
   if (q >= 2 * a.v_hi || j0 >= a.S) return;
   AdamK c = a.c;
@@ -1312,6 +1312,17 @@ template <class GT, class PT>
 static int go_narrow(const StepLaunch& a, int64_t nv, hipStream_t st) {
   const dim3 g((unsigned)((2 * nv + kThreads - 1) / kThreads)), b(kThreads);
   const size_t lds = occupancy_lds(a.n * 4 * GT::bytes > 64 ? kNarrowWideBlocksPerCU : kNarrowBlocksPerCU);
+  if constexpr (GT::bytes == 2) {
+    if (a.n == 64) {
+      // 64 slices: one workgroup of 512 threads per CU, whose eight waves
+      // share their 67 pages (two workgroups of 256 threads touch 134): 42%
+      // fewer first-level translation misses and about 1% faster on the
+      // 7.5B shard
+      const dim3 g2((unsigned)((2 * nv + kNarrow64Threads - 1) / kNarrow64Threads)), b2(kNarrow64Threads);
+      hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 64, kNarrow64Threads>), g2, b2, occupancy_lds(1), st, a);
+      return ZERO_OK;
+    }
+  }
   switch (a.n) {
     case 1: hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 1>), g, b, lds, st, a); return ZERO_OK;
     case 2: hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 2>), g, b, lds, st, a); return ZERO_OK;
@@ -1324,11 +1335,9 @@ static int go_narrow(const StepLaunch& a, int64_t nv, hipStream_t st) {
       break;
     case 16:
     case 32:
-    case 64:
       if constexpr (GT::bytes == 2) {
         if (a.n == 16) hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 16>), g, b, lds, st, a);
-        else if (a.n == 32) hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 32>), g, b, lds, st, a);
-        else hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 64>), g, b, lds, st, a);
+        else hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 32>), g, b, lds, st, a);
         return ZERO_OK;
       }
       break;

@@ -46,6 +46,7 @@ constexpr int kStashBlocksPerCU = 5;  // ... of the update kernel that reads the
 constexpr int kFewStreamBlocksPerCU = 3;  // ... of kernels that sum one or two gradient buffers
 constexpr int kNarrowBlocksPerCU = 3;     // ... of the four-element fused form
 constexpr int kNarrowWideBlocksPerCU = 2; // ... of that form with more than 64 raw gradient bytes per lane
+constexpr int kNarrow64Threads = 512;     // threads per workgroup of that form with 64 16-bit buffers (1 per CU)
 constexpr int kReduceFewBlocksPerCU = 3;  // ... of the reduction pass with at most 128 raw gradient bytes per lane
 constexpr size_t kStaticLdsRoom = 1024;  // LDS left for a streaming kernel's own __shared__ arrays
 constexpr int kSmallThreads = 1024;   // one-workgroup path for small shards ...
