@@ -10,7 +10,8 @@ import torch
 
 import workloads as W
 import zero_sharded_mixed_plan_amd as Z
-from gpu_harness import CODE, oracle_layout, say
+from gpu_harness import CODE, oracle_layout, round_up, say
+from zero_sharded_mixed_plan_amd.optim import StepCtl
 
 pytestmark = pytest.mark.gpu
 
@@ -80,6 +81,50 @@ def test_noalloc_matches_workspace_calls_twice():
     # and once more at the first size, finite
     S3, out3 = _both(big)
     assert _same(S3, out3, "third call") == 0
+
+
+def test_noalloc_full_gradient_and_step_control():
+    """The other arguments it forwards: one full all-reduced gradient read at
+    the rank's pieces (ZeRO-1) of a multi-bucket layout, with the loss scale
+    read from step control in device memory (the inv_scale argument is then
+    ignored).  Same results as the two-call form, bit for bit."""
+    w = W.Workload(name="noalloc_full", tensors=(("a", (70_001,)), ("b", (3,)), ("c", (257, 129)),
+                                                   ("d", (40_000,))),
+                   world=4, rank=2, bucket_cap=60_000, grad_dtype="f16", param_dtype="f16", lr=1e-3,
+                   weight_decay=0.0, steps=1, seed=21, loss_scale=512.0, max_norm=0.5)
+    pl, lay = oracle_layout(w)
+    plan = Z.Plan(W.numels(w.tensors), w.world, w.bucket_cap)
+    assert plan.num_buckets > 1
+    NS = pl.padded_numel
+    ldf = round_up(NS, 64)
+    full = W.make_full_grads(w, NS, lay.tensor_flat_off, 1, step=1, ld=ldf, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    scaler = Z.Scaler(init_scale=w.loss_scale)
+    out = []
+    # (no allocation, step control): the first two runs take the loss scale from
+    # the control block and ignore the inv_scale argument (123); the third passes
+    # 1/512 as the argument and must give the same bits
+    for noalloc, use_ctl in ((True, True), (False, True), (True, False)):
+        ctl = StepCtl(0, w.lr, scaler.s, False, "cuda")
+        g = torch.full((lay.S,), 7.0, dtype=torch.float32, device="cuda")
+        flag = torch.full((1,), 9, dtype=torch.int32, device="cuda")
+        q = torch.full((1,), -1.0, dtype=torch.float64, device="cuda")
+        c = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
+        kw = dict(grad_count=1, grad_layout=Z.ZERO_GRAD_FULL, rank=w.rank, ctl=ctl.ptr if use_ctl else 0)
+        inv = 123.0 if use_ctl else 1.0 / w.loss_scale
+        if noalloc:
+            Z.zero_reduce_norm_noalloc(plan, full.data_ptr(), ldf, CODE["f16"], inv, g.data_ptr(), 0.0,
+                                       w.max_norm, flag.data_ptr(), q.data_ptr(), c.data_ptr(), st, **kw)
+        else:
+            ws = torch.empty(plan.workspace_bytes(), dtype=torch.uint8, device="cuda")
+            Z.zero_reduce_shard(plan, full.data_ptr(), ldf, CODE["f16"], inv, g.data_ptr(), ws.data_ptr(),
+                                True, st, **kw)
+            Z.zero_shard_norm(plan, ws.data_ptr(), 0.0, w.max_norm, flag.data_ptr(), q.data_ptr(),
+                              c.data_ptr(), st)
+        torch.cuda.synchronize()
+        out.append((g.cpu().numpy(), int(flag.item()), q.cpu().numpy(), c.cpu().numpy()))
+    assert _same(lay.S, out[:2], "full gradient, step control") == 0
+    assert _same(lay.S, [out[0], out[2]], "step control against the argument") == 0
 
 
 def test_noalloc_refuses_a_shard_past_the_limit():
