@@ -303,3 +303,18 @@ def test_piece_table_attach_validation():
         assert e.value.code == code, Z.zero_last_error()
     plan.attach_piece_table(0, 0, 0)                          # detaching needs no device
     assert Z.lib().zero_plan_piece_table_bytes(None) == 0
+
+
+def test_noalloc_limit_is_host_arithmetic():
+    """The no-allocation entry point's limit and its refusal need no GPU: the
+    largest shard whose workspace fits the 4 MiB array (one float64 partial and
+    one overflow word per 2048 elements, plus 3 KiB for the finalize) is
+    349,269 tiles; one element more is refused before any HIP call."""
+    cap = Z.zero_noalloc_max_shard()
+    tiles = (Z.ZERO_NOALLOC_SCRATCH_BYTES - 256 * 8 - 256 * 4) // 12
+    assert cap == tiles * 2048 == 715_302_912
+    plan = Z.Plan([cap + 1], 1)
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_reduce_norm_noalloc(plan, 1 << 40, cap + 1, Z.ZERO_BF16, 1.0, 0, 0.0, 1.0, 0, 0, 0)
+    assert e.value.code == Z.ZERO_EINVAL and "fixed array" in Z.zero_last_error()
+    assert str(cap) in Z.zero_last_error()
