@@ -16,7 +16,10 @@
  *   OUT_DIR/fused_{master,m,v,gather}.bin and fused_flag.txt
  *     (zero_adam_step over the slices into separate output state), and
  *   OUT_DIR/clip_{master,m,v,gather}.bin and clip.txt (flag, q, coefficient)
- *     (zero_reduce_shard + zero_shard_norm + zero_adam_step in place).
+ *     (zero_reduce_shard + zero_shard_norm + zero_adam_step in place), and
+ *   OUT_DIR/noalloc_{master,m,v,gather}.bin and noalloc.txt
+ *     (the same clipped step with zero_reduce_norm_noalloc, which takes no
+ *     workspace, on a copy of the inputs).
  * Exit status 0 on success; on any error the message goes to stderr.
  */
 #include <stdint.h>
@@ -208,6 +211,12 @@ int main(int argc, char** argv) {
     fclose(f);
   }
 
+  /* copies of the inputs for the third form, taken before the second updates in place */
+  float* master_n = (float*)dev_copy(master, (size_t)S * 4);
+  float* m_n = (float*)dev_copy(m, (size_t)S * 4);
+  float* v_n = (float*)dev_copy(v, (size_t)S * 4);
+  void* gather3 = dev_copy(gather2, (size_t)padded * pb);
+
   /* 2. the clipped step: reduce (fp32 g + per-tile partials), norm, update in place */
   float* g = NULL;
   void* ws = NULL;
@@ -250,7 +259,39 @@ int main(int argc, char** argv) {
     fclose(f);
   }
 
-  void* bufs[] = {slices, master, m, v, gather, gather2, master_o, m_o, v_o, flag, g, ws, sumsq, coef};
+  /* 3. the clipped step again, its first pass without a workspace */
+  HIP_OK(hipMemset(g, 0xff, (size_t)S * 4));
+  ZERO_OK_OR_DIE(zero_reduce_norm_noalloc(plan, c.rank, slices, c.ld, 0, ZERO_GRAD_SHARD,
+                                          (zero_dtype_t)c.grad_dtype, c.inv_scale, g, 0.0, c.max_norm, flag,
+                                          sumsq, coef, NULL, stream));
+  zero_adam_args_t n = b;
+  n.master_in = master_n;
+  n.m_in = m_n;
+  n.v_in = v_n;
+  n.master_out = master_n;
+  n.m_out = m_n;
+  n.v_out = v_n;
+  n.gather = gather3;
+  ZERO_OK_OR_DIE(zero_adam_step(plan, &n, stream));
+  HIP_OK(hipStreamSynchronize(stream));
+  HIP_OK(hipMemcpy(&h_flag, flag, 4, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(&h_q, sumsq, 8, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(&h_c, coef, 4, hipMemcpyDeviceToHost));
+  save_device(out, "noalloc_master.bin", master_n, (size_t)S * 4);
+  save_device(out, "noalloc_m.bin", m_n, (size_t)S * 4);
+  save_device(out, "noalloc_v.bin", v_n, (size_t)S * 4);
+  save_device(out, "noalloc_gather.bin", gather3, (size_t)padded * pb);
+  {
+    char path[4096];
+    snprintf(path, sizeof path, "%s/noalloc.txt", out);
+    FILE* f = fopen(path, "w");
+    if (!f) die("cannot create", path);
+    fprintf(f, "%u %.17g %.9g\n", h_flag, h_q, (double)h_c);
+    fclose(f);
+  }
+
+  void* bufs[] = {slices, master, m, v, gather, gather2, master_o, m_o, v_o, flag, g, ws, sumsq, coef,
+                  master_n, m_n, v_n, gather3};
   for (size_t i = 0; i < sizeof bufs / sizeof bufs[0]; ++i) HIP_OK(hipFree(bufs[i]));
   HIP_OK(hipStreamDestroy(stream));
   zero_plan_free(plan);

@@ -1,6 +1,7 @@
 """The C ABI from a plain C program (tests/c/abi_step.c: HIP runtime API for
 memory and the stream, no Python or torch in that process): the fused step and
-the clipped step it runs on seeded inputs equal the oracle bit for bit."""
+the clipped step it runs on seeded inputs equal the oracle bit for bit, and the
+clipped step whose first pass takes no workspace equals the clipped step."""
 import dataclasses
 import os
 import subprocess
@@ -95,3 +96,9 @@ def test_c_program_matches_oracle(name, g, p, tmp_path):
     want = gather0.copy()
     OS.write_gather(want, lay.segments, resc.params)
     assert np.array_equal(np.fromfile(out / "clip_gather.bin", dtype=pdt).view(want.dtype), want)
+
+    # the same clipped step with the first pass that takes no workspace: the
+    # same flag, sum of squares and coefficient, and the same outputs bit for bit
+    assert (out / "noalloc.txt").read_text() == (out / "clip.txt").read_text()
+    for fn in ("master.bin", "m.bin", "v.bin", "gather.bin"):
+        assert (out / ("noalloc_" + fn)).read_bytes() == (out / ("clip_" + fn)).read_bytes(), fn

@@ -207,6 +207,17 @@ def test_batch_forms(world, g):
     run_workload(_flat(psi, world, world // 2, g, p, max_norm=0.05), layout=TILED)
 
 
+# Large data-parallel degrees (the deep-dive page's Table 1 goes to N_d = 1024):
+# the runtime-N reduction loop in batches of 16, a world that is not a power
+# of two (an IEEE division), and the last rank, fused and clipped.
+@SIZES
+@pytest.mark.parametrize("world,g", [(128, "bf16"), (257, "f16"), (1024, "bf16")])
+def test_large_world(world, g, S):
+    psi = world * S - 7
+    run_workload(_flat(psi, world, world - 1, g, g), layout=TILED)
+    run_workload(_flat(psi, world, world // 3, g, g, max_norm=0.05), layout=TILED)
+
+
 def test_loss_scaled_fp16():
     run_workload(_flat(64 * 3001, 64, 63, "f16", "f16", loss_scale=65536.0, grad_zero_frac=0.01))
 
