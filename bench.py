@@ -78,8 +78,9 @@ def kernel_source_hash() -> str:
 
 
 def load_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+    """HBM bytes of the kernel's launches in one step (the update of a large
+    shard is several launches) from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
@@ -92,7 +93,7 @@ def load_traffic(kernel: str, workload: str):
     if kv.get("kernel_source_sha256") != kernel_source_hash():
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv["hbm_bytes_per_step"])
     except (KeyError, ValueError):
         return None
 

@@ -256,7 +256,9 @@ typedef struct zero_step_ctl zero_step_ctl_t;
  * [S], 16-byte aligned).  Per 2048-element tile, an overflow word (any
  * non-finite g) and, if want_sumsq, the float64 sum of g^2 go to `ws`
  * (zero_workspace_bytes).  The partition of elements over tiles depends only
- * on S, so the sums are deterministic run to run.
+ * on S, so the sums are deterministic run to run (a shard of more than 2^26
+ * elements is reduced in consecutive launches of at most 2^26 elements; the
+ * partition over tiles is the same).
  * ctl (device zero_step_ctl_t, 8-byte aligned, or NULL): the loss scale is read
  * from it on the device, inv_scale = fp32(1 / ctl->scaler.scale), and the
  * argument inv_scale is ignored (a one-thread launch first writes ctl->k[4];
@@ -351,7 +353,7 @@ typedef struct zero_adam_args {
   const uint32_t* skip_in;   /* NULL, or: nonzero at run time -> state is not written   */
   uint32_t* overflow_out;    /* fused step: 1 if the step was not applied (a non-finite
                                 g, or skip_in set), else 0                              */
-  /* optional hipEvent_t pair recorded around the main update kernel only       */
+  /* optional hipEvent_t pair recorded around the update launches only        */
   void* ev_begin;
   void* ev_end;
   /* optional step control in device memory: lr, step and inv_scale above are
@@ -393,7 +395,10 @@ typedef struct zero_adam_args {
  *    the gather slots are rewritten from master_in (in stash mode they are not
  *    touched).
  * ev_begin/ev_end (hipEvent_t or NULL) are recorded on `stream` immediately
- * before and after the main update kernel.
+ * before and after the update's launches.  A shard of more than 2^26 elements
+ * is updated in consecutive launches of at most 2^26 elements each, in order
+ * on `stream` (large single grids stream measurably slower); the results are
+ * the same as one launch's.
  * ctl != NULL (device zero_step_ctl_t, 8-byte aligned): lr, step and
  * inv_scale come from *ctl (t = ctl->step + 1).  The step's fp32 constants are
  * derived from it on the device before the update and it is advanced after the

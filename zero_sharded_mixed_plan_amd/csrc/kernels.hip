@@ -1367,7 +1367,7 @@ static int dispatch_stash(const StepLaunch& a, zero_dtype_t pt, int64_t nv, hipS
   return fail(ZERO_EINVAL, "unsupported parameter dtype");
 }
 
-int launch_step(const StepLaunch& a, zero_dtype_t gt, zero_dtype_t pt, bool stash, void* stream) {
+static int launch_step_range(const StepLaunch& a, zero_dtype_t gt, zero_dtype_t pt, bool stash, void* stream) {
   const int64_t nv = a.v_hi - a.v_lo;
   if (nv <= 0) return ZERO_OK;
   const unsigned blocks = (unsigned)((nv + kThreads - 1) / kThreads);
@@ -1392,6 +1392,21 @@ int launch_step(const StepLaunch& a, zero_dtype_t gt, zero_dtype_t pt, bool stas
   }
   if (rc != ZERO_OK) return rc;
   return check_launch("step");
+}
+
+// A shard larger than kLaunchElems is updated in consecutive launches of at
+// most that many elements, in order on the stream (see kLaunchElems).
+int launch_step(const StepLaunch& a0, zero_dtype_t gt, zero_dtype_t pt, bool stash, void* stream) {
+  constexpr int64_t kChunk = kLaunchElems / kVec;   // vectors per launch
+  if (a0.v_hi - a0.v_lo <= kChunk) return launch_step_range(a0, gt, pt, stash, stream);
+  StepLaunch a = a0;
+  for (int64_t lo = a0.v_lo; lo < a0.v_hi; lo += kChunk) {
+    a.v_lo = lo;
+    a.v_hi = a0.v_hi - lo < kChunk ? a0.v_hi : lo + kChunk;
+    const int rc = launch_step_range(a, gt, pt, stash, stream);
+    if (rc) return rc;
+  }
+  return ZERO_OK;
 }
 
 template <class GT>
@@ -1479,18 +1494,27 @@ static int reduce_blocks_per_cu(int n, int grad_bytes) {
   return n * kVec * grad_bytes <= 128 ? kReduceFewBlocksPerCU : kStreamBlocksPerCU;
 }
 
-int launch_reduce(const ReduceLaunch& a, zero_dtype_t gt, int64_t nblocks, void* stream) {
+// Tiles [a.blk0, a.blk0 + nblocks), in launches of at most kLaunchElems
+// elements (kLaunchElems / kTile workgroups), in order on the stream.
+int launch_reduce(const ReduceLaunch& a0, zero_dtype_t gt, int64_t nblocks, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int gb = gt == ZERO_F32 ? 4 : 2;
-  const size_t lds = occupancy_lds(reduce_blocks_per_cu(a.n, gb));
-  const dim3 grid((unsigned)nblocks);
-  switch (gt) {
-    case ZERO_F32: go_reduce<TF32>(a, grid, lds, st); break;
-    case ZERO_BF16: go_reduce<TBF16>(a, grid, lds, st); break;
-    case ZERO_F16: go_reduce<TF16>(a, grid, lds, st); break;
-    default: return fail(ZERO_EINVAL, "unsupported gradient dtype");
+  const size_t lds = occupancy_lds(reduce_blocks_per_cu(a0.n, gb));
+  constexpr int64_t kChunk = kLaunchElems / kTile;   // workgroups per launch
+  ReduceLaunch a = a0;
+  for (int64_t done = 0; done < nblocks; done += kChunk) {
+    a.blk0 = a0.blk0 + done;
+    const dim3 grid((unsigned)(nblocks - done < kChunk ? nblocks - done : kChunk));
+    switch (gt) {
+      case ZERO_F32: go_reduce<TF32>(a, grid, lds, st); break;
+      case ZERO_BF16: go_reduce<TBF16>(a, grid, lds, st); break;
+      case ZERO_F16: go_reduce<TF16>(a, grid, lds, st); break;
+      default: return fail(ZERO_EINVAL, "unsupported gradient dtype");
+    }
+    const int rc = check_launch("reduce");
+    if (rc) return rc;
   }
-  return check_launch("reduce");
+  return ZERO_OK;
 }
 
 int launch_norm(const NormLaunch& a, void* stream) {

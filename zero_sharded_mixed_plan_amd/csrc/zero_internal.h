@@ -49,6 +49,13 @@ constexpr int kNarrowWideBlocksPerCU = 2; // ... of that form with more than 64 
 constexpr int kNarrow64Threads = 512;     // threads per workgroup of that form with 64 16-bit buffers (1 per CU)
 constexpr int kReduceFewBlocksPerCU = 3;  // ... of the reduction pass with at most 128 raw gradient bytes per lane
 constexpr size_t kStaticLdsRoom = 1024;  // LDS left for a streaming kernel's own __shared__ arrays
+// Elements per launch of the streaming kernels: a larger shard is processed in
+// consecutive launches of this size on the caller's stream.  Measured with both
+// builds alternating on the same buffers: a single launch over the Llama-7B
+// shard (842M elements, 411K workgroups) streams 5% slower than the same
+// work as 13 launches of 2^26 elements; the clipped Llama-3 step gains 1%;
+// 2^23-2^24 per launch lose more to each launch's ramp and tail than they gain.
+constexpr int64_t kLaunchElems = int64_t(1) << 26;
 constexpr int kSmallThreads = 1024;   // one-workgroup path for small shards ...
 constexpr int64_t kSmallShard = (int64_t)kSmallThreads * kVec;  // ... of at most this many elements
 
