@@ -70,6 +70,14 @@ __device__ __forceinline__ Raw<T> ld_raw(const char* p) {
   return r;
 }
 
+// An empty asm that reads and writes the registers of r: code that uses r
+// cannot be placed ahead of it.
+template <class T>
+__device__ __forceinline__ void pin_raw(Raw<T>& r) {
+#pragma unroll
+  for (int i = 0; i < T::bytes / 2; ++i) asm volatile("" : "+v"(r.q[i].x), "+v"(r.q[i].y), "+v"(r.q[i].z), "+v"(r.q[i].w));
+}
+
 __device__ __forceinline__ float bf16_lo(u32 w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(u32 w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float f16_bits(u32 h) {
@@ -200,6 +208,22 @@ __device__ __forceinline__ float average_unscale(float acc, int n_pow2, float nf
                                                  float inv_scale) {
   const float g = n_pow2 ? acc * recip_n : acc / nf;
   return g * inv_scale;
+}
+
+// The same for K elements, with the choice between the two quotients made once.
+// Written per element, the choice became a branch per element, and the
+// compiler deferred each element's sum into its own branch: every loaded slice
+// then stayed in registers until the last element's turn.
+template <int K>
+__device__ __forceinline__ void average_unscale_k(const float (&acc)[K], float (&g)[K], int n_pow2, float nf,
+                                                  float recip_n, float inv_scale) {
+  if (n_pow2) {
+#pragma unroll
+    for (int e = 0; e < K; ++e) g[e] = (acc[e] * recip_n) * inv_scale;
+  } else {
+#pragma unroll
+    for (int e = 0; e < K; ++e) g[e] = (acc[e] / nf) * inv_scale;
+  }
 }
 
 __device__ __forceinline__ void adamw1(float& p, float& m, float& v, float g, const AdamK& c) {
@@ -344,12 +368,54 @@ __device__ __forceinline__ void add_batch(const Raw<T> (&r)[NB], bool first, flo
   }
 }
 
+// The windowed sum: slice K is added, then the load of slice K + WIN goes out,
+// so a lane keeps WIN slice loads in flight rather than a whole batch; after()
+// runs with the add that follows the last slice load (the caller's state loads
+// go there).  A compile-time recursion, so every register array index is a
+// constant, with a scheduling barrier after each step to keep that order.
+template <class T, int N, int WIN, int K, class F>
+__device__ __forceinline__ void window8(Raw<T> (&r)[N], const char* ubase, int64_t ld_bytes, uint32_t toff,
+                                        float acc[8], F& after) {
+  if constexpr (K < N) {
+    pin_raw<T>(r[K]);   // slice K is widened here, not earlier
+    float w[8];
+    widen8<T>(r[K], w);
+    if constexpr (K == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = w[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + w[e];
+    }
+    // the sum so far is pinned here: otherwise the compiler may defer these
+    // adds past a branch in after() and so issue the whole window at once
+#pragma unroll
+    for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(acc[e]));
+    if constexpr (K + WIN < N) r[K + WIN] = ld_raw<T>(ubase + (int64_t)(K + WIN) * ld_bytes + toff);
+    if constexpr (K + WIN == N) after();
+    __builtin_amdgcn_sched_barrier(0);
+    window8<T, N, WIN, K + 1>(r, ubase, ld_bytes, toff, acc, after);
+  }
+}
+
 // after_last_issue() runs once, right after the loads of the last batch are
-// issued (the caller's state loads go there).
-template <class T, int NB, int NBATCH, class F>
+// issued (the caller's state loads go there).  With a window WIN of fewer than
+// N = NB * NBATCH slices, the windowed sum above instead.
+template <class T, int NB, int NBATCH, int WIN, class F>
 __device__ __forceinline__ void reduce8_fixed(const char* ubase, int64_t ld_bytes, uint32_t toff,
                                               float acc[8], F&& after_last_issue) {
   static_assert(NBATCH >= 1, "at least one batch");
+  constexpr int N = NB * NBATCH;
+  if constexpr (WIN > 0 && WIN < N) {
+    Raw<T> w[N];
+#pragma unroll
+    for (int k = 0; k < WIN; ++k) {   // issued in slice order: the waits count loads in order
+      w[k] = ld_raw<T>(ubase + (int64_t)k * ld_bytes + toff);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    window8<T, N, WIN, 0>(w, ubase, ld_bytes, toff, acc, after_last_issue);
+    return;
+  }
   Raw<T> r[2][NB];
   load_batch<T, NB>(r[0], ubase, ld_bytes, toff);
   if (NBATCH == 1) after_last_issue();
@@ -517,12 +583,12 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
       constexpr int NB = Batch<GT, WIDE>::value;
       float acc[8];
       if constexpr (NBATCH > 0) {
-        // the state loads go out with the last batch of slices, so they hold
-        // no registers while the earlier batches stream in
+        // the state loads go out once the last slice load has been issued, so
+        // they hold no registers while the earlier slices stream in
         const char* ubase = static_cast<const char*>(a.grad) +
                             (a.v_lo + (int64_t)blockIdx.x * kThreads) * (kVec * GT::bytes);
-        reduce8_fixed<GT, NB, NBATCH>(ubase, a.ld_bytes, threadIdx.x * (uint32_t)(kVec * GT::bytes), acc,
-                                      [&]() {
+        reduce8_fixed<GT, NB, NBATCH, kStepWindow>(ubase, a.ld_bytes, threadIdx.x * (uint32_t)(kVec * GT::bytes),
+                                                   acc, [&]() {
                                         load_state();
                                         if constexpr (kLateSegs) sr = wave_segs_v(a, v);
                                       });
@@ -531,11 +597,9 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
         if (a.grad_full) reduce8_pieces<GT, NB>(a, sr, j0, acc);
         else reduce8<GT, NB>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes, a.n, acc);
       }
+      average_unscale_k<8>(acc, g, a.n_pow2, a.nf, a.recip_n, inv_scale);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, inv_scale);
-        bad |= !__builtin_isfinite(g[e]);
-      }
+      for (int e = 0; e < 8; ++e) bad |= !__builtin_isfinite(g[e]);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) adamw1(p[e], m[e], s[e], g[e], c);
@@ -703,16 +767,49 @@ template <> __device__ __forceinline__ void widen4<TF32>(const Raw4<TF32>& r, fl
   o[2] = __uint_as_float(r.q.z); o[3] = __uint_as_float(r.q.w);
 }
 
+// The windowed sum: slice K is added, then the load of slice K + WIN goes out,
+// so a lane keeps WIN slice loads in flight instead of all C; the state loads
+// go out with the add that follows the last slice load.  A compile-time
+// recursion, so that every index into the register arrays is a constant, with
+// a scheduling barrier after each step to keep that order.
+template <class GT, int C, int WIN, int K>
+__device__ __forceinline__ void window_sum(Raw4<GT> (&r)[C], float (&acc)[4], const char* base, int64_t ld,
+                                           const StepLaunch& a, int64_t o0, float (&p)[4], float (&m)[4],
+                                           float (&v)[4]) {
+  if constexpr (K < C) {
+    if constexpr (K == 0) {
+      widen4<GT>(r[0], acc);
+    } else {
+      float w[4];
+      widen4<GT>(r[K], w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = acc[e] + w[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(acc[e]));   // the sum so far, pinned here
+    if constexpr (K + WIN < C) r[K + WIN] = ld_raw4<GT>(base + (int64_t)(K + WIN) * ld);
+    if constexpr (K + WIN == C) {
+      ld4(a.p_in + o0, p);
+      ld4(a.m_in + o0, m);
+      ld4(a.v_in + o0, v);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    window_sum<GT, C, WIN, K + 1>(r, acc, base, ld, a, o0, p, m, v);
+  }
+}
+
 // The fused update over C [S] gradient buffers, four elements per lane as in
 // the stash-mode update: one load per buffer and one each of master, m and v,
-// all issued before the first add, then the same sum (ascending k), arithmetic
-// and stores as the eight-element form.  A lane holds half the bytes in flight
-// of that form, which streams faster for most counts (GPT-2 1.5B shard: one
-// stored output -4%, N = 2 -3%, N = 4 -12%, N = 32 -8%; 7.5B N = 64 -2%;
-// Llama-7B N = 16 -6%; fp32 gradients -8 to -11%).  Lane t takes elements
-// [4 q, 4 q + 4), q = 2 v_lo + t.
-template <class GT, class PT, int C, int TPB = kThreads>
+// then the same sum (ascending k), arithmetic and stores as the eight-element
+// form.  A lane holds half the bytes in flight of that form, which streams
+// faster for most counts (GPT-2 1.5B shard: one stored output -4%, N = 2 -3%,
+// N = 4 -12%, N = 32 -8%; 7.5B N = 64 -2%; Llama-7B N = 16 -6%; fp32 gradients
+// -8 to -11%).  With WIN = 0 every load is issued before the first add; with
+// WIN > 0 (64 buffers) the windowed sum above keeps WIN slice loads in flight.
+// Lane t takes elements [4 q, 4 q + 4), q = 2 v_lo + t.
+template <class GT, class PT, int C, int TPB = kThreads, int WIN = 0>
 __global__ __launch_bounds__(TPB) void narrow_step_kernel(const StepLaunch a) {
+  static_assert(WIN == 0 || (WIN > 0 && WIN < C), "the window holds fewer loads than there are buffers");
   if (a.skip_in != nullptr && *a.skip_in != 0u) {
     if (a.overflow != nullptr && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.overflow, 1u);
     return;
@@ -727,27 +824,40 @@ __global__ __launch_bounds__(TPB) void narrow_step_kernel(const StepLaunch a) {
   bool bad = false;
   if (j0 + 4 <= a.S) {
     const char* base = static_cast<const char*>(a.grad) + j0 * GT::bytes;
-    Raw4<GT> r[C];
-#pragma unroll
-    for (int k = 0; k < C; ++k) r[k] = ld_raw4<GT>(base + (int64_t)k * a.ld_bytes);
     const int64_t o0 = state_off(a, j0);
-    float p[4], m[4], v[4], acc[4], w[4];
-    ld4(a.p_in + o0, p);
-    ld4(a.m_in + o0, m);
-    ld4(a.v_in + o0, v);
-    const SegRange sr = wave_segs(a, w0 * 4, (w0 + 64) * 4);   // behind the loads
-    widen4<GT>(r[0], acc);
+    Raw4<GT> r[C];
+    float p[4], m[4], v[4], acc[4];
+    SegRange sr;
+    if constexpr (WIN > 0) {
+      sr = wave_segs(a, w0 * 4, (w0 + 64) * 4);   // scalar work, ahead of the window
 #pragma unroll
-    for (int k = 1; k < C; ++k) {
-      widen4<GT>(r[k], w);
+      for (int k = 0; k < WIN; ++k) {   // issued in slice order: the waits count loads in order
+        r[k] = ld_raw4<GT>(base + (int64_t)k * a.ld_bytes);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      window_sum<GT, C, WIN, 0>(r, acc, base, a.ld_bytes, a, o0, p, m, v);
+    } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = acc[e] + w[e];
+      for (int k = 0; k < C; ++k) r[k] = ld_raw4<GT>(base + (int64_t)k * a.ld_bytes);
+      ld4(a.p_in + o0, p);
+      ld4(a.m_in + o0, m);
+      ld4(a.v_in + o0, v);
+      sr = wave_segs(a, w0 * 4, (w0 + 64) * 4);   // behind the loads
+      widen4<GT>(r[0], acc);
+#pragma unroll
+      for (int k = 1; k < C; ++k) {
+        float w[4];
+        widen4<GT>(r[k], w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = acc[e] + w[e];
+      }
     }
+    float g[4];
+    average_unscale_k<4>(acc, g, a.n_pow2, a.nf, a.recip_n, inv_scale);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float g = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, inv_scale);
-      bad |= !__builtin_isfinite(g);
-      adamw1(p[e], m[e], v[e], g, c);
+      bad |= !__builtin_isfinite(g[e]);
+      adamw1(p[e], m[e], v[e], g[e], c);
     }
     st4(a.p_out + o0, p);
     st4(a.m_out + o0, m);
@@ -887,8 +997,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_step_kernel(const StepLau
     else
       reduce8<GT, Batch<GT, false>::value>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes,
                                            a.n, acc);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, inv_scale);
+    average_unscale_k<8>(acc, g, a.n_pow2, a.nf, a.recip_n, inv_scale);
   } else {
     for (int e = 0; e < 8; ++e) {
       g[e] = 0.0f;
@@ -1006,18 +1115,16 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) 
       float acc[8], g[8];
       if constexpr (NBATCH > 0) {
         const char* ubase = static_cast<const char*>(a.grad) + blk * (kTile * GT::bytes);
-        reduce8_fixed<GT, NB, NBATCH>(ubase, a.ld_bytes, threadIdx.x * (uint32_t)(kVec * GT::bytes), acc,
-                                      [] {});
+        reduce8_fixed<GT, NB, NBATCH, kReduceWindow>(ubase, a.ld_bytes, threadIdx.x * (uint32_t)(kVec * GT::bytes),
+                                                     acc, [] {});
       } else if (a.grad_full) {
         reduce8_pieces<GT, NB>(a, sr, j0, acc);
       } else {
         reduce8<GT, NB>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes, a.n, acc);
       }
+      average_unscale_k<8>(acc, g, a.n_pow2, a.nf, a.recip_n, inv_scale);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        g[e] = average_unscale(acc[e], a.n_pow2, a.nf, a.recip_n, inv_scale);
-        bad |= !__builtin_isfinite(g[e]);
-      }
+      for (int e = 0; e < 8; ++e) bad |= !__builtin_isfinite(g[e]);
       if (a.g_out != nullptr) st8_stream(a.g_out + j0, g);
       if (a.want_sumsq) {
 #pragma unroll
@@ -1314,12 +1421,11 @@ static int go_narrow(const StepLaunch& a, int64_t nv, hipStream_t st) {
   const size_t lds = occupancy_lds(a.n * 4 * GT::bytes > 64 ? kNarrowWideBlocksPerCU : kNarrowBlocksPerCU);
   if constexpr (GT::bytes == 2) {
     if (a.n == 64) {
-      // 64 slices: one workgroup of 512 threads per CU, whose eight waves
-      // share their 67 pages (two workgroups of 256 threads touch 134): 42%
-      // fewer first-level translation misses and about 1% faster on the
-      // 7.5B shard
+      // 64 slices: one workgroup of 512 threads per CU, each lane with a
+      // window of kNarrow64Window slice loads in flight
       const dim3 g2((unsigned)((2 * nv + kNarrow64Threads - 1) / kNarrow64Threads)), b2(kNarrow64Threads);
-      hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 64, kNarrow64Threads>), g2, b2, occupancy_lds(1), st, a);
+      hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 64, kNarrow64Threads, kNarrow64Window>), g2, b2,
+                         occupancy_lds(1), st, a);
       return ZERO_OK;
     }
   }

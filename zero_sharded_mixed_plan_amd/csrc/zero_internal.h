@@ -48,6 +48,12 @@ constexpr int kNarrowBlocksPerCU = 3;     // ... of the four-element fused form
 constexpr int kNarrowWideBlocksPerCU = 2; // ... of that form with more than 64 raw gradient bytes per lane
 constexpr int kNarrow64Threads = 512;     // threads per workgroup of that form with 64 16-bit buffers (1 per CU)
 constexpr int kReduceFewBlocksPerCU = 3;  // ... of the reduction pass with at most 128 raw gradient bytes per lane
+// Slice loads a lane keeps in flight in the windowed sums, rather than one load
+// per slice all issued at once.  Measured with the builds alternating on the
+// same buffers; a window one or two slices smaller or larger was slower.
+constexpr int kStepWindow = 6;       // eight-element fused update (8 bf16 slices: +2% on Llama-7B and GPT-2 shards)
+constexpr int kReduceWindow = 4;     // eight-element reduction pass (16 bf16 slices: +0.5%)
+constexpr int kNarrow64Window = 8;   // four-element form with 64 16-bit buffers (+1.3%)
 constexpr size_t kStaticLdsRoom = 1024;  // LDS left for a streaming kernel's own __shared__ arrays
 // Elements per launch of the streaming kernels: a larger shard is processed in
 // consecutive launches of this size on the caller's stream.  Measured with both
