@@ -59,7 +59,7 @@ constexpr size_t kStaticLdsRoom = 1024;  // LDS left for a streaming kernel's ow
 // consecutive launches of this size on the caller's stream.  Measured with both
 // builds alternating on the same buffers: a single launch over the Llama-7B
 // shard (842M elements, 411K workgroups) streams 5% slower than the same
-// work as 13 launches of 2^26 elements; the clipped Llama-3 step gains 1%;
+// work as 13 launches of 2^26 elements; the clipped Llama-3 step gains 1-2%;
 // 2^23-2^24 per launch lose more to each launch's ramp and tail than they gain.
 constexpr int64_t kLaunchElems = int64_t(1) << 26;
 constexpr int kSmallThreads = 1024;   // one-workgroup path for small shards ...
