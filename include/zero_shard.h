@@ -396,9 +396,10 @@ typedef struct zero_adam_args {
  *    touched).
  * ev_begin/ev_end (hipEvent_t or NULL) are recorded on `stream` immediately
  * before and after the update's launches.  A shard of more than 2^26 elements
- * is updated in consecutive launches of at most 2^26 elements each, in order
- * on `stream` (large single grids stream measurably slower); the results are
- * the same as one launch's.
+ * (2^23 with 64 16-bit gradient buffers in the shard layout) is updated in
+ * consecutive launches of at most that many elements each, in order on
+ * `stream` (large single grids stream measurably slower); the results are the
+ * same as one launch's.
  * ctl != NULL (device zero_step_ctl_t, 8-byte aligned): lr, step and
  * inv_scale come from *ctl (t = ctl->step + 1).  The step's fp32 constants are
  * derived from it on the device before the update and it is advanced after the

@@ -1500,10 +1500,12 @@ static int launch_step_range(const StepLaunch& a, zero_dtype_t gt, zero_dtype_t 
   return check_launch("step");
 }
 
-// A shard larger than kLaunchElems is updated in consecutive launches of at
-// most that many elements, in order on the stream (see kLaunchElems).
+// A shard larger than kLaunchElems (kLaunchElems64 for the 64-buffer
+// four-element form) is updated in consecutive launches of at most that many
+// elements, in order on the stream.
 int launch_step(const StepLaunch& a0, zero_dtype_t gt, zero_dtype_t pt, bool stash, void* stream) {
-  constexpr int64_t kChunk = kLaunchElems / kVec;   // vectors per launch
+  const bool n64 = !stash && gt != ZERO_F32 && a0.n == 64 && narrow_form(gt, a0.n, a0.grad_full);
+  const int64_t kChunk = (n64 ? kLaunchElems64 : kLaunchElems) / kVec;   // vectors per launch
   if (a0.v_hi - a0.v_lo <= kChunk) return launch_step_range(a0, gt, pt, stash, stream);
   StepLaunch a = a0;
   for (int64_t lo = a0.v_lo; lo < a0.v_hi; lo += kChunk) {

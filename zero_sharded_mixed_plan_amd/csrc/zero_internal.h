@@ -62,6 +62,11 @@ constexpr size_t kStaticLdsRoom = 1024;  // LDS left for a streaming kernel's ow
 // work as 13 launches of 2^26 elements; the clipped Llama-3 step gains 1-2%;
 // 2^23-2^24 per launch lose more to each launch's ramp and tail than they gain.
 constexpr int64_t kLaunchElems = int64_t(1) << 26;
+// The four-element form with 64 16-bit buffers (154 bytes per element) streams
+// best in shorter launches: on the 7.5B N = 64 shard 2^23 elements per launch
+// (14 launches) are 2.5% faster than 2^26, 2^22 and 2^24 about 2%, 2^21 0.5%
+// slower; the eight-slice steps lose 1-8% at 2^23-2^25.
+constexpr int64_t kLaunchElems64 = int64_t(1) << 23;
 constexpr int kSmallThreads = 1024;   // one-workgroup path for small shards ...
 constexpr int64_t kSmallShard = (int64_t)kSmallThreads * kVec;  // ... of at most this many elements
 
