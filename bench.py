@@ -413,6 +413,9 @@ def run(name, steps, warmup, with_cpu, copy_gbps=None, ld_pad=0):
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "bytes_per_element": k_bpe,
+                     # achieved and traffic cover all of the kernel's launches in one
+                     # step: a large shard is updated in several launches
+                     "per": "step",
                      "traffic": traffic},
     }
     if with_cpu:
