@@ -194,10 +194,11 @@ def test_world_and_alignment(world, rank, psi):
 
 
 # Every compiled form of the slice reduction: 1, 2 and 4 slices in one batch of
-# exactly that many, 8 in one narrow batch (fp32: two batches of 4), 16 / 32 /
-# 64 in wide batches (fp32: 8 per batch), and 3 and 24, which no batch size
-# divides (the runtime-N form), each in the fused update and in the clipped
-# path's reduction.
+# exactly that many; 8 (fp32: two batches of 4) and 16 / 32 / 64 (fp32: 8 per
+# batch) in the windowed sum, which keeps a few slice loads in flight (6 in the
+# eight-element update, 4 in the reduction, 8 in the 64-buffer four-element
+# form); and 3 and 24, which no batch size divides (the runtime-N form); each in
+# the fused update and in the clipped path's reduction.
 @pytest.mark.parametrize("world", [1, 2, 3, 4, 8, 16, 24, 32, 64])
 @pytest.mark.parametrize("g", ["f32", "bf16", "f16"])
 def test_batch_forms(world, g):
