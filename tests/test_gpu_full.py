@@ -122,6 +122,81 @@ def test_full_size(name):
     del A, B, gather, slices
 
 
+# Shards just past the library's launch size (2^26 elements per launch; 2^23
+# for the 64-buffer four-element form), so that a step runs as two launches
+# with a short, ragged second one: the eight-element fused update (8 bf16
+# slices, S = 8 mod 8 + 5), the 64-buffer form (S = 2 mod 4) and the clipped
+# path (reduction of 16 bf16 slices, then the stash update).  Every element
+# against the oracle, as above.
+BOUNDARY_CASES = {
+    "step8": dict(world=8, S=(1 << 26) + 3 * 2048 + 5, g="bf16", clip=False, loss_scale=1.0),
+    "narrow64": dict(world=64, S=(1 << 23) + 2048 + 6, g="f16", clip=False, loss_scale=1024.0),
+    "clip16": dict(world=16, S=(1 << 26) + 2048 + 7, g="bf16", clip=True, loss_scale=1.0),
+}
+
+
+@pytest.mark.parametrize("case", list(BOUNDARY_CASES))
+def test_launch_boundaries(case):
+    cfg = BOUNDARY_CASES[case]
+    N, S_want = cfg["world"], cfg["S"]
+    w = W.Workload(name=f"boundary_{case}", tensors=(("flat", (N * S_want - 3,)),), world=N, rank=N - 1,
+                   bucket_cap=0, grad_dtype=cfg["g"], param_dtype=cfg["g"], lr=1e-3, weight_decay=0.1,
+                   loss_scale=cfg["loss_scale"], max_norm=(0.05 if cfg["clip"] else 0.0), steps=1, seed=41,
+                   m_sigma=1e-3, v_sigma=1e-6)
+    pl, lay = oracle_layout(w)
+    S = lay.S
+    assert S == S_want
+    dev = torch.device("cuda")
+    plan = Z.Plan(W.numels(w.tensors), w.world, w.bucket_cap)
+    assert plan.shard_numel == S and plan.segments(w.rank) == lay.segments
+    ld = (S + 63) // 64 * 64
+    say(f"launch boundary {case}: S={S} N={N} ld={ld}")
+    layout = Z.ZERO_STATE_TILED
+    A, B = _tiled_state(w, lay, plan, dev)
+    pdt = W.torch_dtype(w.param_dtype)
+    gather = torch.full((pl.padded_numel,), SENTINEL[w.param_dtype], dtype=pdt, device=dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    slices = W.make_slices(w, lay, step=1, ld=ld, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+    common = dict(rank=w.rank, gather=gather.data_ptr(), param_dtype=CODE[w.param_dtype], lr=w.lr,
+                  beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=w.t0 + 1)
+    c32 = g = None
+    if cfg["clip"]:
+        g = torch.empty(S, dtype=torch.float32, device=dev)
+        ws = torch.empty(plan.workspace_bytes(), dtype=torch.uint8, device=dev)
+        sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+        coef = torch.zeros(1, dtype=torch.float32, device=dev)
+        Z.zero_reduce_shard(plan, slices.data_ptr(), ld, CODE[w.grad_dtype], 1.0 / w.loss_scale,
+                            g.data_ptr(), ws.data_ptr(), True, st)
+        Z.zero_shard_norm(plan, ws.data_ptr(), 0.0, w.max_norm, flag.data_ptr(), sumsq.data_ptr(),
+                          coef.data_ptr(), st)
+        B.copy_(A)
+        a = Z.adam_args(g_stash=g.data_ptr(), clip_coef=coef.data_ptr(), skip_in=flag.data_ptr(),
+                        **state_arg_dict(layout, [B], [B]), **common)
+    else:
+        a = Z.adam_args(grad=slices.data_ptr(), grad_ld=ld, grad_dtype=CODE[w.grad_dtype],
+                        inv_scale=1.0 / w.loss_scale, overflow_out=flag.data_ptr(),
+                        **state_arg_dict(layout, [A], [B]), **common)
+    Z.zero_adam_step(plan, a, st)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    if cfg["clip"]:
+        c32 = F(coef.item())
+    n, oracle_flag, q_ora = check_whole_shard(
+        S=S, w=w, t=w.t0 + 1, grads_of=shard_grads(slices, w.world), state_in=A, state_out=B,
+        gather=gather, segments=lay.segments, flag=0, c32=c32, g_gpu=g,
+        chunk=(1 << 20 if w.world > 16 else 1 << 22), what=f"launch boundary {case}")
+    assert not oracle_flag
+    if cfg["clip"]:
+        q = float(sumsq.item())
+        assert abs(q - q_ora) <= 1e-9 * q_ora, (q, q_ora)
+        assert c32 == OS.clip_coefficient(q, w.max_norm)
+    say(f"  every element of [0, {n}) equal to the oracle bit for bit")
+    assert outside_slots_untouched(gather, lay.segments, SENTINEL[w.param_dtype]), "write outside the slots"
+    assert tail_intact(A, S) and tail_intact(B, S), "tiled state written past S"
+    del A, B, gather, slices
+
+
 # The benchmark's other forms of the GPT-2 step, at full size: one stored
 # reduce-scatter output, one full all-reduced gradient (ZeRO-1), the
 # per-parameter dim-0 layout (580 pieces), and the reduction pass alone.
