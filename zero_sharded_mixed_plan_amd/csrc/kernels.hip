@@ -805,7 +805,8 @@ __device__ __forceinline__ void window_sum(Raw4<GT> (&r)[C], float (&acc)[4], co
 // faster for most counts (GPT-2 1.5B shard: one stored output -4%, N = 2 -3%,
 // N = 4 -12%, N = 32 -8%; 7.5B N = 64 -2%; Llama-7B N = 16 -6%; fp32 gradients
 // -8 to -11%).  With WIN = 0 every load is issued before the first add; with
-// WIN > 0 (64 buffers) the windowed sum above keeps WIN slice loads in flight.
+// WIN > 0 (16, 32 and 64 buffers) the windowed sum above keeps WIN slice loads
+// in flight.
 // Lane t takes elements [4 q, 4 q + 4), q = 2 v_lo + t.
 template <class GT, class PT, int C, int TPB = kThreads, int WIN = 0>
 __global__ __launch_bounds__(TPB) void narrow_step_kernel(const StepLaunch a) {
@@ -1422,9 +1423,9 @@ static int go_narrow(const StepLaunch& a, int64_t nv, hipStream_t st) {
   if constexpr (GT::bytes == 2) {
     if (a.n == 64) {
       // 64 slices: one workgroup of 512 threads per CU, each lane with a
-      // window of kNarrow64Window slice loads in flight
+      // window of kNarrowWindow slice loads in flight
       const dim3 g2((unsigned)((2 * nv + kNarrow64Threads - 1) / kNarrow64Threads)), b2(kNarrow64Threads);
-      hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 64, kNarrow64Threads, kNarrow64Window>), g2, b2,
+      hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 64, kNarrow64Threads, kNarrowWindow>), g2, b2,
                          occupancy_lds(1), st, a);
       return ZERO_OK;
     }
@@ -1442,8 +1443,8 @@ static int go_narrow(const StepLaunch& a, int64_t nv, hipStream_t st) {
     case 16:
     case 32:
       if constexpr (GT::bytes == 2) {
-        if (a.n == 16) hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 16>), g, b, lds, st, a);
-        else hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 32>), g, b, lds, st, a);
+        if (a.n == 16) hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 16, kThreads, kNarrowWindow>), g, b, lds, st, a);
+        else hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 32, kThreads, kNarrowWindow>), g, b, lds, st, a);
         return ZERO_OK;
       }
       break;
