@@ -559,11 +559,9 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
   // The wave's pieces are needed for the parameter stores only, except where
   // the gradient itself is read at gather offsets (the runtime-N form).  With
   // many pieces their search is a chain of dependent argument loads, so in the
-  // compile-time batch form it runs after the vector loads have been issued,
-  // hidden behind them (the FSDP2 layout of GPT-2: -2%) -- except with four
-  // batches, where the registers are all taken by the slices in flight and the
-  // search state would spill.
-  constexpr bool kLateSegs = NBATCH == 1 || NBATCH == 2;
+  // compile-time form it runs after the slice loads have been issued, hidden
+  // behind them (the FSDP2 layout of GPT-2: -2%).
+  constexpr bool kLateSegs = NBATCH > 0;
   SegRange sr{0, -1};
   if constexpr (!kLateSegs) sr = wave_segs_v(a, v);
   AdamK c = a.c;
@@ -805,8 +803,8 @@ __device__ __forceinline__ void window_sum(Raw4<GT> (&r)[C], float (&acc)[4], co
 // faster for most counts (GPT-2 1.5B shard: one stored output -4%, N = 2 -3%,
 // N = 4 -12%, N = 32 -8%; 7.5B N = 64 -2%; Llama-7B N = 16 -6%; fp32 gradients
 // -8 to -11%).  With WIN = 0 every load is issued before the first add; with
-// WIN > 0 (16, 32 and 64 buffers) the windowed sum above keeps WIN slice loads
-// in flight.
+// WIN > 0 (16, 32 and 64 16-bit buffers, 8 fp32 ones) the windowed sum above
+// keeps WIN slice loads in flight.
 // Lane t takes elements [4 q, 4 q + 4), q = 2 v_lo + t.
 template <class GT, class PT, int C, int TPB = kThreads, int WIN = 0>
 __global__ __launch_bounds__(TPB) void narrow_step_kernel(const StepLaunch a) {
@@ -1316,10 +1314,9 @@ int launch_ctl_end(zero_step_ctl_t* ctl, const u32* flag, void* stream) {
   return check_launch("step control (end)");
 }
 
-// Batches of N / NB known at compile time for the world sizes that are a
-// whole number (1, 2 or 4) of batches and that the narrow form does not take:
-// 16-bit N = 8 in one narrow batch, fp32 N = 16 and 32 in two and four wide
-// ones; the runtime-N form for every other N and for the full-gradient source.
+// The compile-time form (the windowed sum) for the one count the narrow form
+// does not take in the shard layout, 16-bit N = 8; the runtime-N form for
+// every other N and for the full-gradient source.
 template <class GT, class PT, bool WIDE>
 static void go_step_full(const StepLaunch& a, unsigned blocks, size_t lds, hipStream_t st) {
   constexpr int NB = Batch<GT, WIDE>::value;
@@ -1328,16 +1325,6 @@ static void go_step_full(const StepLaunch& a, unsigned blocks, size_t lds, hipSt
   if constexpr (GT::bytes == 2 && !WIDE) {
     if (nbatch == 1) {
       hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 1>), g, b, lds, st, a);
-      return;
-    }
-  }
-  if constexpr (GT::bytes == 4 && WIDE) {
-    if (nbatch == 2) {
-      hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 2>), g, b, lds, st, a);
-      return;
-    }
-    if (nbatch == 4) {
-      hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 4>), g, b, lds, st, a);
       return;
     }
   }
@@ -1406,14 +1393,16 @@ static int dispatch_pt(const StepLaunch& a, zero_dtype_t pt, unsigned blocks, hi
 }
 
 // The narrow fused form serves the shard layout when its buffer count is
-// compiled: 1, 2, 4, and 16, 32, 64 for 16-bit gradients or 8 for fp32 (the
-// eight-element form keeps 16-bit N = 8, where the two measure the same, and
-// fp32 N >= 16).  Resident workgroups per CU: 3, or 2 when a lane's raw
-// gradient bytes exceed 64, as measured.
+// compiled: 1, 2, 4, and 16, 32, 64 for 16-bit gradients or 8, 16, 32 for fp32
+// (the eight-element form keeps 16-bit N = 8, where the windowed eight-element
+// sum is faster, and fp32 N = 64).  fp32 N = 16 with a window of 4 slice loads
+// runs 8% faster than the eight-element form's two windowed batches (GPT-2
+// tensors).  Resident workgroups per CU: 3, or 2 when a lane's raw gradient
+// bytes exceed 64, as measured.
 static bool narrow_form(zero_dtype_t gt, int n, int grad_full) {
   if (grad_full) return false;
   if (n == 1 || n == 2 || n == 4) return true;
-  return gt == ZERO_F32 ? n == 8 : (n == 16 || n == 32 || n == 64);
+  return gt == ZERO_F32 ? (n == 8 || n == 16 || n == 32) : (n == 16 || n == 32 || n == 64);
 }
 
 template <class GT, class PT>
@@ -1436,18 +1425,18 @@ static int go_narrow(const StepLaunch& a, int64_t nv, hipStream_t st) {
     case 4: hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 4>), g, b, lds, st, a); return ZERO_OK;
     case 8:
       if constexpr (GT::bytes == 4) {
-        hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 8>), g, b, lds, st, a);
+        hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 8, kThreads, kNarrowWindow32>), g, b, lds, st, a);
         return ZERO_OK;
       }
       break;
     case 16:
+      hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 16, kThreads, GT::bytes == 4 ? kNarrowWindow32 : kNarrowWindow>), g,
+                         b, lds, st, a);
+      return ZERO_OK;
     case 32:
-      if constexpr (GT::bytes == 2) {
-        if (a.n == 16) hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 16, kThreads, kNarrowWindow>), g, b, lds, st, a);
-        else hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 32, kThreads, kNarrowWindow>), g, b, lds, st, a);
-        return ZERO_OK;
-      }
-      break;
+      hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 32, kThreads, GT::bytes == 4 ? kNarrowWindow32 : kNarrowWindow>), g,
+                         b, lds, st, a);
+      return ZERO_OK;
   }
   return fail(ZERO_EINVAL, "narrow fused form: no compiled buffer count " + std::to_string(a.n));
 }

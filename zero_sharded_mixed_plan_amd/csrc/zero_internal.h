@@ -54,6 +54,7 @@ constexpr int kReduceFewBlocksPerCU = 3;  // ... of the reduction pass with at m
 constexpr int kStepWindow = 6;       // eight-element fused update (8 bf16 slices: +2% on Llama-7B and GPT-2 shards)
 constexpr int kReduceWindow = 4;     // eight-element reduction pass (16 bf16 slices: +0.5%)
 constexpr int kNarrowWindow = 8;     // four-element form with 16, 32 or 64 16-bit buffers (+2.8%, +0.7%, +1.3%)
+constexpr int kNarrowWindow32 = 4;   // four-element form with 8, 16 or 32 fp32 buffers (N = 8: +2.5%)
 constexpr size_t kStaticLdsRoom = 1024;  // LDS left for a streaming kernel's own __shared__ arrays
 // Elements per launch of the streaming kernels: a larger shard is processed in
 // consecutive launches of this size on the caller's stream.  Measured with both
