@@ -796,6 +796,108 @@ __device__ __forceinline__ void window_sum(Raw4<GT> (&r)[C], float (&acc)[4], co
   }
 }
 
+// The windowed sum for a buffer count n known only at run time, n >= WIN: a
+// ring of WIN registers (slice k lives in r[k mod WIN]).  The running sum starts
+// at -0, the identity of the addition, so every step is the same add.  Steps
+// k < n - WIN add slice k and load slice k + WIN into the freed register; they
+// run as a loop over whole groups of WIN steps (every ring index a constant)
+// and a tail selected by rho = (n - WIN) mod WIN: rho more such steps, the
+// state loads, then the WIN steps that only add.  No load is under a branch
+// inside a group, so each add waits for its own slice only.
+template <class GT>
+__device__ __forceinline__ void ring_add(const Raw4<GT>& r, float (&acc)[4]) {
+  float w[4];
+  widen4<GT>(r, w);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = acc[e] + w[e];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(acc[e]));   // the sum so far, pinned here
+}
+
+// steps I .. E - 1 of a group: add r[I], load slice k0 + I + WIN into r[I]
+template <class GT, int WIN, int I, int E>
+__device__ __forceinline__ void ring_load_steps(Raw4<GT> (&r)[WIN], float (&acc)[4], const char* base, int64_t ld,
+                                                int k0) {
+  if constexpr (I < E) {
+    ring_add<GT>(r[I], acc);
+    r[I] = ld_raw4<GT>(base + (int64_t)(k0 + I + WIN) * ld);
+    __builtin_amdgcn_sched_barrier(0);
+    ring_load_steps<GT, WIN, I + 1, E>(r, acc, base, ld, k0);
+  }
+}
+
+// the last WIN steps, from ring phase R: add only
+template <class GT, int WIN, int R, int J>
+__device__ __forceinline__ void ring_drain(Raw4<GT> (&r)[WIN], float (&acc)[4]) {
+  if constexpr (J < WIN) {
+    ring_add<GT>(r[(R + J) % WIN], acc);
+    __builtin_amdgcn_sched_barrier(0);
+    ring_drain<GT, WIN, R, J + 1>(r, acc);
+  }
+}
+
+template <class GT, int WIN, int R>
+__device__ __forceinline__ void ring_tail(Raw4<GT> (&r)[WIN], float (&acc)[4], const char* base, int64_t ld, int k0,
+                                          const StepLaunch& a, int64_t o0, float (&p)[4], float (&m)[4],
+                                          float (&v)[4]) {
+  ring_load_steps<GT, WIN, 0, R>(r, acc, base, ld, k0);
+  ld4(a.p_in + o0, p);
+  ld4(a.m_in + o0, m);
+  ld4(a.v_in + o0, v);
+  __builtin_amdgcn_sched_barrier(0);
+  ring_drain<GT, WIN, R, 0>(r, acc);
+}
+
+template <class GT, int WIN, int R>
+__device__ __forceinline__ void ring_tail_sel(int rho, Raw4<GT> (&r)[WIN], float (&acc)[4], const char* base,
+                                              int64_t ld, int k0, const StepLaunch& a, int64_t o0, float (&p)[4],
+                                              float (&m)[4], float (&v)[4]) {
+  if constexpr (R < WIN) {
+    if (rho == R) {
+      ring_tail<GT, WIN, R>(r, acc, base, ld, k0, a, o0, p, m, v);
+      return;
+    }
+    ring_tail_sel<GT, WIN, R + 1>(rho, r, acc, base, ld, k0, a, o0, p, m, v);
+  }
+}
+
+template <class GT, int WIN>
+__device__ __forceinline__ void window_sum_rt(const char* base, int64_t ld, int n, float (&acc)[4],
+                                              const StepLaunch& a, int64_t o0, float (&p)[4], float (&m)[4],
+                                              float (&v)[4]) {
+  Raw4<GT> r[WIN];
+#pragma unroll
+  for (int i = 0; i < WIN; ++i) {   // issued in slice order: the waits count loads in order
+    r[i] = ld_raw4<GT>(base + (int64_t)i * ld);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = -0.0f;
+  const int groups = (n - WIN) / WIN;
+  int k0 = 0;
+  for (int gi = 0; gi < groups; ++gi, k0 += WIN) ring_load_steps<GT, WIN, 0, WIN>(r, acc, base, ld, k0);
+  ring_tail_sel<GT, WIN, 0>((n - WIN) % WIN, r, acc, base, ld, k0, a, o0, p, m, v);
+}
+
+// A run-time count n < WIN: every load at once, then the adds.
+template <class GT, int WIN>
+__device__ __forceinline__ void small_sum_rt(const char* base, int64_t ld, int n, float (&acc)[4],
+                                             const StepLaunch& a, int64_t o0, float (&p)[4], float (&m)[4],
+                                             float (&v)[4]) {
+  Raw4<GT> r[WIN];
+#pragma unroll
+  for (int i = 0; i < WIN; ++i)
+    if (i < n) r[i] = ld_raw4<GT>(base + (int64_t)i * ld);
+  ld4(a.p_in + o0, p);
+  ld4(a.m_in + o0, m);
+  ld4(a.v_in + o0, v);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = -0.0f;
+#pragma unroll
+  for (int i = 0; i < WIN; ++i)
+    if (i < n) ring_add<GT>(r[i], acc);
+}
+
 // The fused update over C [S] gradient buffers, four elements per lane as in
 // the stash-mode update: one load per buffer and one each of master, m and v,
 // then the same sum (ascending k), arithmetic and stores as the eight-element
@@ -808,7 +910,8 @@ __device__ __forceinline__ void window_sum(Raw4<GT> (&r)[C], float (&acc)[4], co
 // Lane t takes elements [4 q, 4 q + 4), q = 2 v_lo + t.
 template <class GT, class PT, int C, int TPB = kThreads, int WIN = 0>
 __global__ __launch_bounds__(TPB) void narrow_step_kernel(const StepLaunch a) {
-  static_assert(WIN == 0 || (WIN > 0 && WIN < C), "the window holds fewer loads than there are buffers");
+  static_assert(WIN == 0 || (WIN > 0 && (C == 0 || WIN < C)), "the window holds fewer loads than there are buffers");
+  static_assert(C > 0 || WIN > 0, "a run-time buffer count takes the windowed sum");
   if (a.skip_in != nullptr && *a.skip_in != 0u) {
     if (a.overflow != nullptr && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.overflow, 1u);
     return;
@@ -824,10 +927,14 @@ __global__ __launch_bounds__(TPB) void narrow_step_kernel(const StepLaunch a) {
   if (j0 + 4 <= a.S) {
     const char* base = static_cast<const char*>(a.grad) + j0 * GT::bytes;
     const int64_t o0 = state_off(a, j0);
-    Raw4<GT> r[C];
     float p[4], m[4], v[4], acc[4];
     SegRange sr;
-    if constexpr (WIN > 0) {
+    if constexpr (C == 0) {   // the buffer count a.n, known at run time
+      sr = wave_segs(a, w0 * 4, (w0 + 64) * 4);
+      if (a.n >= WIN) window_sum_rt<GT, WIN>(base, a.ld_bytes, a.n, acc, a, o0, p, m, v);
+      else small_sum_rt<GT, WIN>(base, a.ld_bytes, a.n, acc, a, o0, p, m, v);
+    } else if constexpr (WIN > 0) {
+      Raw4<GT> r[C];
       sr = wave_segs(a, w0 * 4, (w0 + 64) * 4);   // scalar work, ahead of the window
 #pragma unroll
       for (int k = 0; k < WIN; ++k) {   // issued in slice order: the waits count loads in order
@@ -836,6 +943,7 @@ __global__ __launch_bounds__(TPB) void narrow_step_kernel(const StepLaunch a) {
       }
       window_sum<GT, C, WIN, 0>(r, acc, base, a.ld_bytes, a, o0, p, m, v);
     } else {
+      Raw4<GT> r[C];
 #pragma unroll
       for (int k = 0; k < C; ++k) r[k] = ld_raw4<GT>(base + (int64_t)k * a.ld_bytes);
       ld4(a.p_in + o0, p);
@@ -874,7 +982,7 @@ __global__ __launch_bounds__(TPB) void narrow_step_kernel(const StepLaunch a) {
     for (int64_t j = j0; j < a.S; ++j) {
       const int64_t oj = state_off(a, j);
       float pe = a.p_in[oj], me = a.m_in[oj], ve = a.v_in[oj];
-      const float acc = reduce1<GT>(static_cast<const char*>(a.grad) + j * GT::bytes, a.ld_bytes, C);
+      const float acc = reduce1<GT>(static_cast<const char*>(a.grad) + j * GT::bytes, a.ld_bytes, C > 0 ? C : a.n);
       const float g = average_unscale(acc, a.n_pow2, a.nf, a.recip_n, inv_scale);
       bad |= !__builtin_isfinite(g);
       adamw1(pe, me, ve, g, c);
@@ -1401,8 +1509,7 @@ static int dispatch_pt(const StepLaunch& a, zero_dtype_t pt, unsigned blocks, hi
 // bytes exceed 64, as measured.
 static bool narrow_form(zero_dtype_t gt, int n, int grad_full) {
   if (grad_full) return false;
-  if (n == 1 || n == 2 || n == 4) return true;
-  return gt == ZERO_F32 ? (n == 8 || n == 16 || n == 32) : (n == 16 || n == 32 || n == 64);
+  return !(n == 8 && gt != ZERO_F32);
 }
 
 template <class GT, class PT>
@@ -1438,7 +1545,10 @@ static int go_narrow(const StepLaunch& a, int64_t nv, hipStream_t st) {
                          b, lds, st, a);
       return ZERO_OK;
   }
-  return fail(ZERO_EINVAL, "narrow fused form: no compiled buffer count " + std::to_string(a.n));
+  // any other count: the run-time windowed sum
+  hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 0, kThreads, GT::bytes == 4 ? kNarrowWindow32 : kNarrowWindow>), g, b,
+                     lds, st, a);
+  return ZERO_OK;
 }
 
 template <class GT>
