@@ -432,6 +432,73 @@ __device__ __forceinline__ void reduce8_fixed(const char* ubase, int64_t ld_byte
   }
 }
 
+// The same windowed sum for a count n >= WIN known only at run time: a ring
+// of WIN registers (slice k in r[k mod WIN]), whole groups of WIN steps in a
+// loop, then one of WIN straight-line tails chosen by rho = (n - WIN) mod WIN:
+// rho more steps that load, after(), and the WIN steps that only add.  The sum
+// starts at -0, the identity of the addition, so every step is the same add
+// and the result is that of the ordered sum bit for bit.
+template <class T>
+__device__ __forceinline__ void ring_add8(Raw<T>& r, float acc[8]) {
+  float w[8];
+  widen8<T>(r, w);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = acc[e] + w[e];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(acc[e]));
+}
+
+template <class T, int WIN, int I, int E>
+__device__ __forceinline__ void ring8_load_steps(Raw<T> (&r)[WIN], float acc[8], const char* base, int64_t ld,
+                                                 int k0) {
+  if constexpr (I < E) {
+    ring_add8<T>(r[I], acc);
+    r[I] = ld_raw<T>(base + (int64_t)(k0 + I + WIN) * ld);
+    __builtin_amdgcn_sched_barrier(0);
+    ring8_load_steps<T, WIN, I + 1, E>(r, acc, base, ld, k0);
+  }
+}
+
+template <class T, int WIN, int R, int J>
+__device__ __forceinline__ void ring8_drain(Raw<T> (&r)[WIN], float acc[8]) {
+  if constexpr (J < WIN) {
+    ring_add8<T>(r[(R + J) % WIN], acc);
+    __builtin_amdgcn_sched_barrier(0);
+    ring8_drain<T, WIN, R, J + 1>(r, acc);
+  }
+}
+
+template <class T, int WIN, int R, class F>
+__device__ __forceinline__ void ring8_tail_sel(int rho, Raw<T> (&r)[WIN], float acc[8], const char* base, int64_t ld,
+                                               int k0, F& after) {
+  if constexpr (R < WIN) {
+    if (rho == R) {
+      ring8_load_steps<T, WIN, 0, R>(r, acc, base, ld, k0);
+      after();
+      __builtin_amdgcn_sched_barrier(0);
+      ring8_drain<T, WIN, R, 0>(r, acc);
+      return;
+    }
+    ring8_tail_sel<T, WIN, R + 1>(rho, r, acc, base, ld, k0, after);
+  }
+}
+
+template <class T, int WIN, class F>
+__device__ __forceinline__ void reduce8_ring(const char* base, int64_t ld, int n, float acc[8], F&& after) {
+  Raw<T> r[WIN];
+#pragma unroll
+  for (int i = 0; i < WIN; ++i) {   // issued in slice order: the waits count loads in order
+    r[i] = ld_raw<T>(base + (int64_t)i * ld);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = -0.0f;
+  const int groups = (n - WIN) / WIN;
+  int k0 = 0;
+  for (int gi = 0; gi < groups; ++gi, k0 += WIN) ring8_load_steps<T, WIN, 0, WIN>(r, acc, base, ld, k0);
+  ring8_tail_sel<T, WIN, 0>((n - WIN) % WIN, r, acc, base, ld, k0, after);
+}
+
 template <class T>
 __device__ __forceinline__ float reduce1(const char* base, int64_t ld_bytes, int n) {
   float acc = ld_one<T>(base);
@@ -1226,6 +1293,9 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) 
                                                      acc, [] {});
       } else if (a.grad_full) {
         reduce8_pieces<GT, NB>(a, sr, j0, acc);
+      } else if (a.n >= kReduceWindow) {   // the windowed sum with a run-time count
+        reduce8_ring<GT, kReduceWindow>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes, a.n, acc,
+                                        [] {});
       } else {
         reduce8<GT, NB>(static_cast<const char*>(a.grad) + j0 * GT::bytes, a.ld_bytes, a.n, acc);
       }
