@@ -193,19 +193,34 @@ def test_world_and_alignment(world, rank, psi):
     run_workload(_flat(psi, world, rank, "bf16", "bf16"), layout=TILED)
 
 
-# Every compiled form of the slice reduction: 1, 2 and 4 slices in one batch of
-# exactly that many; 8 (fp32: two batches of 4) and 16 / 32 / 64 (fp32: 8 per
-# batch) in the windowed sum, which keeps a few slice loads in flight (6 in the
-# eight-element update, 4 in the reduction, 8 in the 64-buffer four-element
-# form); and 3 and 24, which no batch size divides (the runtime-N form); each in
-# the fused update and in the clipped path's reduction.
-@pytest.mark.parametrize("world", [1, 2, 3, 4, 8, 16, 24, 32, 64])
+# Every form of the slice sum, in the fused update and in the clipped path's
+# reduction, at a shard of 10,007 elements: above the one-workgroup path's
+# limit (8192), so the multi-workgroup kernels run, over five state tiles with
+# a ragged end.  The fused update: 1, 2, 4 buffers at once; 16-bit 8 in the
+# eight-element windowed sum; 16-bit 16, 32, 64 and fp32 8, 16, 32 in the
+# compiled four-element windows; every other count in the run-time ring, whose
+# tail differs with (N - W) mod W (W = 8 for 16-bit, 4 for fp32): the counts
+# 9-15 and 17 reach every tail of the 16-bit ring, 5-7 and 9-11 those of the
+# fp32 one, 3 the path below the window.  The reduction: 1, 2, 4, 8, 16, 32,
+# 64 compiled (fp32 8 as two batches of 4), the other counts of four or more
+# in its ring (W = 4), 3 in the runtime loop.
+@pytest.mark.parametrize("world", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 24, 32, 48, 64])
 @pytest.mark.parametrize("g", ["f32", "bf16", "f16"])
 def test_batch_forms(world, g):
-    psi = world * 4099
+    psi = world * 10007
     p = "bf16" if g != "f32" else "f32"
     run_workload(_flat(psi, world, world - 1, g, p), layout=TILED)
     run_workload(_flat(psi, world, world // 2, g, p, max_norm=0.05), layout=TILED)
+
+
+# The one-workgroup path (a shard of at most 8192 elements) sums any count in
+# its runtime loop: a few counts, fused and clipped.
+@pytest.mark.parametrize("world", [3, 8, 24, 64])
+@pytest.mark.parametrize("g", ["f32", "bf16"])
+def test_small_path_counts(world, g):
+    psi = world * 4099
+    run_workload(_flat(psi, world, world - 1, g, g), layout=TILED)
+    run_workload(_flat(psi, world, world // 2, g, g, max_norm=0.05), layout=TILED)
 
 
 # Large data-parallel degrees (the deep-dive page's Table 1 goes to N_d = 1024):
