@@ -1588,10 +1588,10 @@ static int go_narrow(const StepLaunch& a, int64_t nv, hipStream_t st) {
   const size_t lds = occupancy_lds(a.n * 4 * GT::bytes > 64 ? kNarrowWideBlocksPerCU : kNarrowBlocksPerCU);
   if constexpr (GT::bytes == 2) {
     if (a.n == 64) {
-      // 64 slices: one workgroup of 512 threads per CU, each lane with a
-      // window of kNarrowWindow slice loads in flight
+      // 64 slices: one workgroup of kNarrow64Threads per CU, each lane with a
+      // window of kNarrow64Window slice loads in flight
       const dim3 g2((unsigned)((2 * nv + kNarrow64Threads - 1) / kNarrow64Threads)), b2(kNarrow64Threads);
-      hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 64, kNarrow64Threads, kNarrowWindow>), g2, b2,
+      hipLaunchKernelGGL((narrow_step_kernel<GT, PT, 64, kNarrow64Threads, kNarrow64Window>), g2, b2,
                          occupancy_lds(1), st, a);
       return ZERO_OK;
     }

@@ -46,14 +46,19 @@ constexpr int kStashBlocksPerCU = 5;  // ... of the update kernel that reads the
 constexpr int kFewStreamBlocksPerCU = 3;  // ... of kernels that sum one or two gradient buffers
 constexpr int kNarrowBlocksPerCU = 3;     // ... of the four-element fused form
 constexpr int kNarrowWideBlocksPerCU = 2; // ... of that form with more than 64 raw gradient bytes per lane
-constexpr int kNarrow64Threads = 512;     // threads per workgroup of that form with 64 16-bit buffers (1 per CU)
+constexpr int kNarrow64Threads = 1024;    // threads per workgroup of that form with 64 16-bit buffers (1 per CU)
 constexpr int kReduceFewBlocksPerCU = 3;  // ... of the reduction pass with at most 128 raw gradient bytes per lane
 // Slice loads a lane keeps in flight in the windowed sums, rather than one load
 // per slice all issued at once.  Measured with the builds alternating on the
 // same buffers; a window one or two slices smaller or larger was slower.
 constexpr int kStepWindow = 6;       // eight-element fused update (8 bf16 slices: +2% on Llama-7B and GPT-2 shards)
 constexpr int kReduceWindow = 4;     // eight-element reduction pass (16 bf16 slices: +0.5%)
-constexpr int kNarrowWindow = 8;     // four-element form with 16, 32 or 64 16-bit buffers (+2.8%, +0.7%, +1.3%)
+constexpr int kNarrowWindow = 8;     // four-element form with 16 or 32 16-bit buffers (+2.8%, +0.7%)
+// ... with 64 16-bit buffers, at 16 waves per CU: against 8 waves with a
+// window of 8 (itself +1.3% over all at once), +1.2% and +3.6% on two parts; a
+// window of 4 +0.6% and +2.5%, 5 or 6 -4 to -5% (48 wave-wide slice loads in
+// flight per CU, against 64 before and 80 at a window of 5)
+constexpr int kNarrow64Window = 3;
 constexpr int kNarrowWindow32 = 4;   // four-element form with 8, 16 or 32 fp32 buffers (N = 8: +2.5%)
 constexpr size_t kStaticLdsRoom = 1024;  // LDS left for a streaming kernel's own __shared__ arrays
 // Elements per launch of the streaming kernels: a larger shard is processed in
