@@ -213,6 +213,19 @@ def test_batch_forms(world, g):
     run_workload(_flat(psi, world, world // 2, g, p, max_norm=0.05), layout=TILED)
 
 
+# Exact zeros of either sign in every slice (at a quarter of those positions -0
+# in all slices, so the sum there is -0).  The oracle sums from slice 0; the
+# windowed sums start from -0, which leaves every value unchanged under IEEE
+# addition, +0 included, so the two agree bit for bit.  The clipped path's
+# stash holds g itself and shows the sign of each zero sum.
+@pytest.mark.parametrize("world", [3, 5, 8, 12, 16, 24, 64])
+@pytest.mark.parametrize("g", ["f32", "bf16"])
+def test_signed_zero_sums(world, g):
+    w = dataclasses.replace(_flat(world * 10007, world, world - 1, g, g), grad_signed_zero_frac=0.3)
+    run_workload(w, layout=TILED)
+    run_workload(dataclasses.replace(w, max_norm=0.05), rank=world // 2, layout=TILED)
+
+
 # The one-workgroup path (a shard of at most 8192 elements) sums any count in
 # its runtime loop: a few counts, fused and clipped.
 @pytest.mark.parametrize("world", [3, 8, 24, 64])

@@ -379,3 +379,34 @@ def test_toy_four_ranks_match_torch_adam():
     diff = max((a - b).abs().max().item() for a, b in zip(ref.parameters(), model.parameters()))
     assert diff < 1e-5, diff
     assert P.state_bytes(pl) == 57_636
+
+
+def test_signed_zero_inputs_and_the_sum_identity():
+    """The generator's signed-zero option (used by the GPU's signed-zero parity
+    cases) yields -0 and +0 at its positions and -0 in every slice at some; and
+    -0 is the identity of IEEE fp32 addition, the fact the windowed sums rely
+    on when they start from -0 instead of from slice 0."""
+    import torch
+    import workloads as W
+    from oracle import plan as OP
+    w = W.Workload(name="sz", tensors=(("x", (12 * 3001,)),), world=12, rank=11, bucket_cap=0,
+                   grad_dtype="bf16", param_dtype="bf16", lr=1e-3, grad_signed_zero_frac=0.3, seed=5)
+    pl = OP.make_plan(W.numels(w.tensors), w.world)
+    lay = W.Layout(S=pl.shard_numel, segments=OP.rank_segments(pl, w.rank), tensor_flat_off=list(pl.tensor_offset))
+    x = W.make_slices(w, lay, step=1).float()
+    zero = x == 0
+    neg = zero & torch.signbit(x)
+    assert neg.any() and (zero & ~torch.signbit(x)).any()
+    assert neg.all(dim=0).any()
+    # the ordered sum from slice 0 equals the sum started at -0, bit for bit
+    xs = x.numpy().astype(F)
+    a = xs[0].copy()
+    b = np.full(xs.shape[1], -0.0, F) + xs[0]
+    for k in range(1, xs.shape[0]):
+        a = a + xs[k]
+        b = b + xs[k]
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.signbit(a[neg.all(dim=0).numpy()]).all()
+    special = np.array([0.0, -0.0, 1e-45, -1e-45, 1.0, -3.5, np.inf, -np.inf, np.nan], F)
+    assert np.array_equal((np.float32(-0.0) + special).view(np.uint32)[:-1], special.view(np.uint32)[:-1])
+    assert np.isnan(np.float32(-0.0) + special[-1])

@@ -104,6 +104,8 @@ class Workload:
     grad_sigma: float = 1e-3       # std of each slice's entries (before loss scaling)
     grad_sigma_loguniform: Optional[Tuple[float, float]] = None  # per-tensor sigma range
     grad_zero_frac: float = 0.0    # fraction of positions exactly 0 in every slice
+    grad_signed_zero_frac: float = 0.0  # fraction of positions that are +0 or -0 in every slice (sign per slice;
+                                        # at a quarter of them -0 in all slices)
     master_sigma: float = 0.02
     m_sigma: float = 0.0           # 0: m starts at 0
     v_sigma: float = 0.0           # 0: v starts at 0; else v = |N(0, v_sigma)|
@@ -178,6 +180,8 @@ def _gen(device, seed: int, stream: int):
 
 
 STREAM_MASTER, STREAM_M, STREAM_V, STREAM_SIGMA, STREAM_ZEROS, STREAM_INF = 1, 2, 3, 4, 5, 6
+STREAM_SZEROS = 7                  # positions of the signed zeros; their signs use STREAM_SIGNS0 + 1000*s + k
+STREAM_SIGNS0 = 20_000_000
 STREAM_SLICE0 = 100  # slice k of step s uses STREAM_SLICE0 + 1000*s + k
 STREAM_FULL0 = 10_000_000  # full gradient k of step s uses STREAM_FULL0 + 1000*s + k
 
@@ -273,6 +277,16 @@ def zero_positions(w: Workload, S: int, device="cpu"):
     return u < w.grad_zero_frac
 
 
+def signed_zero_positions(w: Workload, S: int, device="cpu"):
+    """(Bool [S] of the positions holding a zero of either sign in every slice,
+    Bool [S] of those where every slice holds -0), or None."""
+    import torch
+    if w.grad_signed_zero_frac <= 0:
+        return None
+    u = torch.rand(S, generator=_gen(device, w.seed, STREAM_SZEROS), device=device)
+    return u < w.grad_signed_zero_frac, u < 0.25 * w.grad_signed_zero_frac
+
+
 def inf_position(w: Workload, S: int) -> Tuple[int, int]:
     """(slice, element) of the injected +inf: slice = seed mod N, element ~ U[0, S)."""
     import torch
@@ -299,6 +313,7 @@ def make_slices(w: Workload, lay: Layout, step: int = 1, ld: Optional[int] = Non
         assert out.shape == (w.world, ld) and out.dtype == dt
         out[:, S:].zero_()
     sig = _elem_sigma(w, lay, device) * w.loss_scale
+    szeros = signed_zero_positions(w, S, device)
     zeros = zero_positions(w, S, device)
     pad = pad_mask(lay, device)
     if zeros is not None:
@@ -308,6 +323,12 @@ def make_slices(w: Workload, lay: Layout, step: int = 1, ld: Optional[int] = Non
         x = torch.randn(S, generator=g, device=device, dtype=torch.float32)
         x.mul_(sig)
         x.masked_fill_(pad, 0.0)   # +0 exactly (a product with sigma 0 may be -0)
+        if szeros is not None:
+            sz, all_neg = szeros
+            neg = torch.rand(S, generator=_gen(device, w.seed, STREAM_SIGNS0 + 1000 * step + k),
+                             device=device) < 0.5
+            x.masked_fill_(sz, 0.0)
+            x.masked_fill_(sz & (neg | all_neg) & ~pad, -0.0)
         out[k, :S].copy_(x)
         del x
     if w.inject_inf_step is not None and step == w.inject_inf_step:
