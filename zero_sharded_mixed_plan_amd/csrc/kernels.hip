@@ -1268,8 +1268,9 @@ __device__ __forceinline__ double wave_sum(double x) {
   return x;
 }
 
-// NB slices per load batch, NBATCH batches known at compile time (0: any N,
-// the runtime loop with batches of NB)
+// NB slices per load batch, NBATCH batches known at compile time (0: any N:
+// the run-time ring, or the runtime loop with batches of NB below its window
+// and for the full-gradient source)
 template <class GT, int NB, int NBATCH>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(const ReduceLaunch a) {
   // one 8-element vector per thread; workgroup b owns vectors [256 b, 256 b + 256),
@@ -1509,7 +1510,8 @@ static void go_step_full(const StepLaunch& a, unsigned blocks, size_t lds, hipSt
   hipLaunchKernelGGL((step_kernel<GT, PT, WIDE, 0>), g, b, lds, st, a);
 }
 
-// wide batches when N > 8; the turn-taking reduction when the batch divides N
+// wide batches when N > 8 (the full-gradient source); the windowed sum for
+// 16-bit N = 8
 template <class GT, class PT>
 static void go_step(const StepLaunch& a, unsigned blocks, size_t lds, hipStream_t st) {
   if (a.n > 8)
@@ -1726,11 +1728,13 @@ int launch_recast(const StepLaunch& a, zero_dtype_t pt, const u32* cond, void* s
   return check_launch("recast");
 }
 
-// The reduction's batch forms: every whole number of batches of the usual
+// The reduction's compiled forms: every whole number of batches of the usual
 // size (8 16-bit or 4 fp32 slices, twice that for larger N) in 1, 2 or 4
-// batches, and one batch of exactly N for N = 1, 2, 4 (the runtime loop, with
-// its per-slice guards, reduced 4 bf16 slices of the GPT-2 shard at 3.3 TB/s).
-// Only reachable forms are instantiated.
+// batches, summed in the window of kReduceWindow slice loads, and one batch of
+// exactly N for N = 1, 2, 4 (the runtime loop, with its per-slice guards,
+// reduced 4 bf16 slices of the GPT-2 shard at 3.3 TB/s).  Other counts take
+// the ring (four or more) or the runtime loop (three), inside the NBATCH = 0
+// instantiation.  Only reachable forms are instantiated.
 template <class GT>
 static void go_reduce(const ReduceLaunch& a, dim3 grid, size_t lds, hipStream_t st) {
   const dim3 blk(kThreads);
@@ -1759,7 +1763,8 @@ static void go_reduce(const ReduceLaunch& a, dim3 grid, size_t lds, hipStream_t 
       }
     }
   }
-  // the runtime loop: batches of the usual size, twice that above 8 buffers
+  // the run-time count: the ring, or the runtime loop below the window, with
+  // batches of the usual size, twice that above 8 buffers
   if (n > 8) hipLaunchKernelGGL((reduce_kernel<GT, NW, 0>), grid, blk, lds, st, a);
   else hipLaunchKernelGGL((reduce_kernel<GT, NS, 0>), grid, blk, lds, st, a);
 }
